@@ -1,0 +1,375 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these re-types an oracle formula.  Each compares the oracle with an
+independent route:
+  * library routines (torch.nn.functional.layer_norm, gelu) and autograd;
+  * central finite differences;
+  * the defining statement of the method: the prediction for token i uses the
+    parameters after one gradient step, from the mini-batch-start parameters,
+    on the losses of tokens j <= i of its mini-batch, each weighted by its
+    learning rate ("代码连连看——TTT", compute_mini_batch, primal branch); the
+    step over the whole mini-batch is then carried to the next one;
+  * the pages' claim that the dual branch computes the same thing as the
+    primal branch (same listing; TTTLinear.ttt NOTE on dual/primal);
+  * special cases: mini_batch_size = 1 is online gradient descent; eta = 0
+    leaves the state untouched; cutting a sequence anywhere and carrying the
+    state (TTTBase.forward remainder handling, TTTCache) changes nothing;
+  * rotary embedding: identity at position 0, norm preserving, relative
+    position property, and equal to multiplication by e^{i p theta} on
+    complex pairs.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as Fn
+
+torch.set_default_dtype(torch.float64)
+EPS = 1e-6
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ----------------------------------------------------------------------------
+# LayerNorm forward and fused LN + L2 backward
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("D", [4, 8, 64])
+def test_ln_fwd_matches_library(orc, D):
+    r = _rng(D)
+    for _ in range(5):
+        z = r.normal(size=D) * r.uniform(0.01, 5) + r.normal() * 3
+        gam, bet = r.normal(size=D), r.normal(size=D)
+        ref = Fn.layer_norm(torch.tensor(z), (D,), torch.tensor(gam), torch.tensor(bet), EPS).numpy()
+        np.testing.assert_allclose(orc.ln_fwd(z, gam, bet, EPS), ref, rtol=1e-12, atol=1e-12)
+
+
+def _l2_loss(z, t, gam, bet):
+    return 0.5 * ((Fn.layer_norm(z, (z.shape[-1],), gam, bet, EPS) - t) ** 2).sum()
+
+
+@pytest.mark.parametrize("D", [4, 8, 64])
+def test_ln_l2_grad_finite_differences(orc, D):
+    r = _rng(100 + D)
+    z = r.normal(size=D) * 0.7 + 0.3
+    t, gam, bet = r.normal(size=D), 1 + 0.3 * r.normal(size=D), 0.3 * r.normal(size=D)
+    g = orc.ln_l2_grad(z, t, gam, bet, EPS)
+    h = 1e-6
+    T = lambda a: torch.tensor(a)  # noqa: E731
+    fd = np.empty(D)
+    for c in range(D):
+        zp, zm = z.copy(), z.copy()
+        zp[c] += h
+        zm[c] -= h
+        fd[c] = (_l2_loss(T(zp), T(t), T(gam), T(bet)) - _l2_loss(T(zm), T(t), T(gam), T(bet))).item() / (2 * h)
+    np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("D", [8, 64])
+def test_ln_l2_grad_autograd(orc, D):
+    r = _rng(200 + D)
+    for scale in (0.01, 1.0, 30.0):
+        z = torch.tensor(r.normal(size=D) * scale, requires_grad=True)
+        t, gam, bet = (torch.tensor(r.normal(size=D)) for _ in range(3))
+        (gz,) = torch.autograd.grad(_l2_loss(z, t, gam, bet), z)
+        g = orc.ln_l2_grad(z.detach().numpy(), t.numpy(), gam.numpy(), bet.numpy(), EPS)
+        np.testing.assert_allclose(g, gz.numpy(), rtol=1e-10, atol=1e-12 / scale)
+
+
+# ----------------------------------------------------------------------------
+# Rotary embedding
+# ----------------------------------------------------------------------------
+def _rope_complex(x, p, base=10000.0):
+    """Rotation of the pairs (x_i, x_{i+D/2}) written as complex multiplication."""
+    D = x.shape[-1]
+    h = D // 2
+    zc = x[:h] + 1j * x[h:]
+    ang = p * base ** (-2.0 * np.arange(h) / D)
+    w = zc * np.exp(1j * ang)
+    return np.concatenate([w.real, w.imag])
+
+
+def test_rope_properties(orc):
+    r = _rng(7)
+    D = 64
+    x, y = r.normal(size=D), r.normal(size=D)
+    np.testing.assert_array_equal(orc.rope_row(x, 0), x)
+    for p in (1, 5, 15, 300):
+        xr = orc.rope_row(x, p)
+        assert abs(np.linalg.norm(xr) - np.linalg.norm(x)) < 1e-12
+        np.testing.assert_allclose(xr, _rope_complex(x, p), rtol=1e-12, atol=1e-12)
+    # relative position: <R_m x, R_n y> = <R_{m-n} x, y>
+    for m, n in ((7, 3), (15, 0), (9, 9)):
+        lhs = orc.rope_row(x, m) @ orc.rope_row(y, n)
+        rhs = orc.rope_row(x, m - n) @ y
+        assert abs(lhs - rhs) < 1e-11
+
+
+# ----------------------------------------------------------------------------
+# TTT-Linear: the oracle against the gradient-step definition (autograd)
+# ----------------------------------------------------------------------------
+def _linear_by_autograd(q, k, v, eta, gam, bet, W0, b0, K, offset=0, rope=False, loss_scale=0.5):
+    """Definition of the layer written with autograd.  Block boundaries are at
+    absolute positions that are multiples of K; ``offset`` must be aligned."""
+    assert offset % K == 0
+    L, D = q.shape
+    T = lambda a: torch.tensor(np.asarray(a, dtype=np.float64))  # noqa: E731
+    if rope:
+        q = np.stack([_rope_complex(q[t], (offset + t) % K) for t in range(L)])
+        k = np.stack([_rope_complex(k[t], (offset + t) % K) for t in range(L)])
+    q, k, v, eta, gam, bet = map(T, (q, k, v, eta, gam, bet))
+    W, b = T(W0), T(b0)
+    outs = []
+    for t in range(L):
+        j0 = t - t % K
+        Wp, bp = W.clone().requires_grad_(True), b.clone().requires_grad_(True)
+        loss = 0.0
+        for j in range(j0, t + 1):
+            zj = k[j] @ Wp + bp
+            loss = loss + eta[j] * loss_scale * ((Fn.layer_norm(zj, (D,), gam, bet, EPS) - (v[j] - k[j])) ** 2).sum()
+        gW, gb = torch.autograd.grad(loss, (Wp, bp))
+        Wbar, bbar = W - gW, b - gb
+        outs.append(q[t] + Fn.layer_norm(q[t] @ Wbar + bbar, (D,), gam, bet, EPS))
+        if (t + 1) % K == 0:
+            W, b = Wbar.detach(), bbar.detach()
+    return torch.stack(outs).numpy(), W.numpy(), b.numpy()
+
+
+def _problem(seed, L, D, rich=True):
+    r = _rng(seed)
+    q, k, v = (r.normal(size=(L, D)) for _ in range(3))
+    eta = 1 / (1 + np.exp(-r.normal(size=L))) / 8
+    W0 = r.normal(size=(D, D)) * 0.02
+    if rich:
+        b0 = 0.05 * r.normal(size=D)
+        gam, bet = 1 + 0.2 * r.normal(size=D), 0.2 * r.normal(size=D)
+    else:
+        b0, gam, bet = np.zeros(D), np.ones(D), np.zeros(D)
+    return q, k, v, eta, gam, bet, W0, b0
+
+
+def _run_oracle_linear(orc, q, k, v, eta, gam, bet, W0, b0, K, offset=0, rope=False):
+    D = q.shape[1]
+    W, b, G, gb = W0.copy(), b0.copy(), np.zeros((D, D)), np.zeros(D)
+    out = orc.linear_chain(q, k, v, eta, gam, bet, W, b, G, gb, K=K, offset=offset, rope=rope)
+    return out, W, b, G, gb
+
+
+@pytest.mark.parametrize("D,K,L,rope", [(8, 4, 11, False), (16, 1, 7, False), (64, 16, 40, False),
+                                         (8, 4, 13, True), (64, 16, 35, True)])
+def test_linear_matches_gradient_step_definition(orc, D, K, L, rope):
+    prob = _problem(1000 + D * K + L, L, D)
+    out, W, b, G, gb = _run_oracle_linear(orc, *prob, K=K, rope=rope)
+    ref, Wr, br = _linear_by_autograd(*prob, K=K, rope=rope)
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-10)
+    # state: block-start W, b plus the open block's accumulated gradient
+    if L % K == 0:
+        np.testing.assert_allclose(W, Wr, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(b, br, rtol=1e-10, atol=1e-12)
+        assert not G.any() and not gb.any()
+    else:
+        np.testing.assert_allclose(W, Wr, rtol=1e-10, atol=1e-12)  # committed blocks only
+        assert np.abs(G).max() > 0
+
+
+def test_online_gd_is_minibatch_one(orc):
+    """mini_batch_size = 1: every token is its own mini-batch; the output of
+    token t uses the state after the step on token t itself, and that state is
+    carried — plain online gradient descent."""
+    D, L = 16, 9
+    q, k, v, eta, gam, bet, W0, b0 = _problem(31, L, D)
+    out, W, b, _, _ = _run_oracle_linear(orc, q, k, v, eta, gam, bet, W0, b0, K=1)
+    Wt, bt = torch.tensor(W0), torch.tensor(b0)
+    T = torch.tensor
+    for t in range(L):
+        Wp, bp = Wt.clone().requires_grad_(True), bt.clone().requires_grad_(True)
+        z = T(k[t]) @ Wp + bp
+        loss = 0.5 * ((Fn.layer_norm(z, (D,), T(gam), T(bet), EPS) - T(v[t] - k[t])) ** 2).sum()
+        gW, gb_ = torch.autograd.grad(loss, (Wp, bp))
+        Wt, bt = Wt - eta[t] * gW, bt - eta[t] * gb_
+        o = T(q[t]) + Fn.layer_norm(T(q[t]) @ Wt + bt, (D,), T(gam), T(bet), EPS)
+        np.testing.assert_allclose(out[t], o.numpy(), rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(W, Wt.numpy(), rtol=1e-10, atol=1e-13)
+
+
+def test_loss_constant_reading(orc):
+    """Half-square loss with 2*eta equals full-square loss with eta."""
+    D, K, L = 8, 4, 8
+    q, k, v, eta, gam, bet, W0, b0 = _problem(77, L, D)
+    out, W, b, _, _ = _run_oracle_linear(orc, q, k, v, 2 * eta, gam, bet, W0, b0, K=K)
+    ref, Wr, br = _linear_by_autograd(q, k, v, eta, gam, bet, W0, b0, K=K, loss_scale=1.0)
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(W, Wr, rtol=1e-10, atol=1e-12)
+
+
+def test_eta_zero_closed_form(orc):
+    D, K, L = 64, 16, 37
+    q, k, v, eta, gam, bet, W0, b0 = _problem(5, L, D)
+    out, W, b, G, gb = _run_oracle_linear(orc, q, k, v, 0 * eta, gam, bet, W0, b0, K=K)
+    ref = q + Fn.layer_norm(torch.tensor(q @ W0 + b0), (D,), torch.tensor(gam), torch.tensor(bet), EPS).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(W, W0)
+    np.testing.assert_array_equal(b, b0)
+
+
+@pytest.mark.parametrize("D,K,L,rope", [(8, 4, 16, False), (64, 16, 64, False), (64, 16, 48, True),
+                                         (16, 1, 5, False), (8, 3, 12, True)])
+def test_dual_equals_primal(orc, D, K, L, rope):
+    q, k, v, eta, gam, bet, W0, b0 = _problem(9 + L, L, D)
+    out_p, Wp, bp, _, _ = _run_oracle_linear(orc, q, k, v, eta, gam, bet, W0, b0, K=K, rope=rope)
+    Wd, bd = W0.copy(), b0.copy()
+    out_d = orc.linear_chain_dual(q, k, v, eta, gam, bet, Wd, bd, K=K, rope=rope)
+    np.testing.assert_allclose(out_d, out_p, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(Wd, Wp, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(bd, bp, rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("rope", [False, True])
+def test_split_invariance_every_cut(orc, rope):
+    """Processing [0, s) then [s, L) with the carried state equals [0, L),
+    for every cut s (remainder handling and TTTCache continuation)."""
+    D, K, L = 64, 16, 64
+    q, k, v, eta, gam, bet, W0, b0 = _problem(42, L, D)
+    whole, Ww, bw, _, _ = _run_oracle_linear(orc, q, k, v, eta, gam, bet, W0, b0, K=K, rope=rope)
+    for s in range(1, L):
+        W, b, G, gb = W0.copy(), b0.copy(), np.zeros((D, D)), np.zeros(D)
+        o1 = orc.linear_chain(q[:s], k[:s], v[:s], eta[:s], gam, bet, W, b, G, gb, K=K, offset=0, rope=rope)
+        o2 = orc.linear_chain(q[s:], k[s:], v[s:], eta[s:], gam, bet, W, b, G, gb, K=K, offset=s, rope=rope)
+        np.testing.assert_allclose(np.concatenate([o1, o2]), whole, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(W, Ww, rtol=1e-12, atol=1e-14)
+
+
+def test_prefill_then_single_token_decode(orc):
+    D, K, L, P = 64, 16, 80, 24
+    q, k, v, eta, gam, bet, W0, b0 = _problem(8, L, D)
+    whole, Ww, bw, Gw, gbw = _run_oracle_linear(orc, q, k, v, eta, gam, bet, W0, b0, K=K)
+    W, b, G, gb = W0.copy(), b0.copy(), np.zeros((D, D)), np.zeros(D)
+    outs = [orc.linear_chain(q[:P], k[:P], v[:P], eta[:P], gam, bet, W, b, G, gb, K=K)]
+    for t in range(P, L):
+        outs.append(orc.linear_chain(q[t:t + 1], k[t:t + 1], v[t:t + 1], eta[t:t + 1], gam, bet, W, b, G, gb,
+                                     K=K, offset=t))
+    np.testing.assert_allclose(np.concatenate(outs), whole, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(W, Ww, rtol=1e-12, atol=1e-14)
+
+
+def test_batch_driver_matches_chains(orc):
+    B, H, L, D, K = 2, 3, 20, 8, 4
+    r = _rng(3)
+    XQ, XK, XV = (r.normal(size=(B, H, L, D)) for _ in range(3))
+    eta = r.uniform(0, 0.1, size=(H, L))
+    lw, lb = 1 + 0.1 * r.normal(size=(H, D)), 0.1 * r.normal(size=(H, D))
+    W0 = r.normal(size=(H, D, D)) * 0.02
+    W = np.ascontiguousarray(np.broadcast_to(W0, (B, H, D, D)))
+    b = np.zeros((B, H, D))
+    G, gb = np.zeros_like(W), np.zeros_like(b)
+    out = orc.linear_batch(XQ, XK, XV, eta, 0, lw, lb, W, b, G, gb, K=K, rope=True)
+    for bi in range(B):
+        for h in range(H):
+            Wc, bc, Gc, gbc = W0[h].copy(), np.zeros(D), np.zeros((D, D)), np.zeros(D)
+            oc = orc.linear_chain(XQ[bi, h], XK[bi, h], XV[bi, h], eta[h], lw[h], lb[h], Wc, bc, Gc, gbc,
+                                  K=K, rope=True)
+            np.testing.assert_array_equal(out[bi, h], oc)
+            np.testing.assert_array_equal(W[bi, h], Wc)
+            np.testing.assert_array_equal(G[bi, h], Gc)
+
+
+# ----------------------------------------------------------------------------
+# TTT-MLP
+# ----------------------------------------------------------------------------
+def test_gelu_matches_library(orc):
+    xs = np.linspace(-6, 6, 97)
+    for x in xs:
+        xt = torch.tensor(x, requires_grad=True)
+        y = Fn.gelu(xt, approximate="none")
+        (dy,) = torch.autograd.grad(y, xt)
+        assert abs(orc.gelu(x) - y.item()) < 1e-14
+        assert abs(orc.gelu_grad(x) - dy.item()) < 1e-13
+
+
+def _mlp_problem(seed, L, D, F):
+    r = _rng(seed)
+    q, k, v = (r.normal(size=(L, D)) for _ in range(3))
+    eta = 1 / (1 + np.exp(-r.normal(size=L))) / 8
+    W1, W2 = r.normal(size=(D, F)) * 0.2, r.normal(size=(F, D)) * 0.2
+    b1, b2 = 0.05 * r.normal(size=F), 0.05 * r.normal(size=D)
+    gam, bet = 1 + 0.2 * r.normal(size=D), 0.2 * r.normal(size=D)
+    return q, k, v, eta, gam, bet, W1, b1, W2, b2
+
+
+def _run_oracle_mlp(orc, q, k, v, eta, gam, bet, W1, b1, W2, b2, K, offset=0, rope=False):
+    D, F = W1.shape
+    st = [W1.copy(), b1.copy(), W2.copy(), b2.copy(), np.zeros((D, F)), np.zeros(F), np.zeros((F, D)), np.zeros(D)]
+    out = orc.mlp_chain(q, k, v, eta, gam, bet, *st, K=K, offset=offset, rope=rope)
+    return out, st
+
+
+def _mlp_by_autograd(q, k, v, eta, gam, bet, W1, b1, W2, b2, K):
+    L, D = q.shape
+    T = lambda a: torch.tensor(np.asarray(a, dtype=np.float64))  # noqa: E731
+    q, k, v, eta, gam, bet = map(T, (q, k, v, eta, gam, bet))
+    P = [T(W1), T(b1), T(W2), T(b2)]
+
+    def f(x, p):
+        return Fn.gelu(x @ p[0] + p[1], approximate="none") @ p[2] + p[3]
+
+    outs = []
+    for t in range(L):
+        j0 = t - t % K
+        Pp = [p.clone().requires_grad_(True) for p in P]
+        loss = 0.0
+        for j in range(j0, t + 1):
+            loss = loss + eta[j] * 0.5 * ((Fn.layer_norm(f(k[j], Pp), (D,), gam, bet, EPS) - (v[j] - k[j])) ** 2).sum()
+        grads = torch.autograd.grad(loss, Pp)
+        Pbar = [p - g for p, g in zip(P, grads)]
+        outs.append(q[t] + Fn.layer_norm(f(q[t], Pbar), (D,), gam, bet, EPS))
+        if (t + 1) % K == 0:
+            P = [p.detach() for p in Pbar]
+    return torch.stack(outs).numpy(), [p.numpy() for p in P]
+
+
+@pytest.mark.parametrize("D,F,K,L", [(8, 16, 4, 10), (64, 256, 16, 32), (8, 32, 1, 5)])
+def test_mlp_matches_gradient_step_definition(orc, D, F, K, L):
+    prob = _mlp_problem(D + F + L, L, D, F)
+    out, st = _run_oracle_mlp(orc, *prob, K=K)
+    ref, Pr = _mlp_by_autograd(*prob, K=K)
+    np.testing.assert_allclose(out, ref, rtol=1e-9, atol=1e-10)
+    for a, b in zip(st[:4], Pr):
+        np.testing.assert_allclose(a, b, rtol=1e-9, atol=1e-12)
+
+
+@pytest.mark.parametrize("D,F,K,L,rope", [(8, 16, 4, 12, False), (64, 256, 16, 32, True)])
+def test_mlp_dual_equals_primal(orc, D, F, K, L, rope):
+    q, k, v, eta, gam, bet, W1, b1, W2, b2 = _mlp_problem(5 + L, L, D, F)
+    out_p, st = _run_oracle_mlp(orc, q, k, v, eta, gam, bet, W1, b1, W2, b2, K=K, rope=rope)
+    sd = [W1.copy(), b1.copy(), W2.copy(), b2.copy()]
+    out_d = orc.mlp_chain_dual(q, k, v, eta, gam, bet, *sd, K=K, rope=rope)
+    np.testing.assert_allclose(out_d, out_p, rtol=1e-10, atol=1e-11)
+    for a, b in zip(sd, st[:4]):
+        np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-13)
+
+
+def test_mlp_split_invariance(orc):
+    D, F, K, L = 8, 16, 4, 14
+    q, k, v, eta, gam, bet, W1, b1, W2, b2 = _mlp_problem(99, L, D, F)
+    whole, stw = _run_oracle_mlp(orc, q, k, v, eta, gam, bet, W1, b1, W2, b2, K=K)
+    for s in range(1, L):
+        st = [W1.copy(), b1.copy(), W2.copy(), b2.copy(), np.zeros((D, F)), np.zeros(F), np.zeros((F, D)),
+              np.zeros(D)]
+        o1 = orc.mlp_chain(q[:s], k[:s], v[:s], eta[:s], gam, bet, *st, K=K, offset=0)
+        o2 = orc.mlp_chain(q[s:], k[s:], v[s:], eta[s:], gam, bet, *st, K=K, offset=s)
+        np.testing.assert_allclose(np.concatenate([o1, o2]), whole, rtol=1e-12, atol=1e-12)
+        for a, b in zip(st, stw):
+            np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+
+
+def test_mlp_eta_zero_closed_form(orc):
+    D, F, K, L = 8, 16, 4, 9
+    q, k, v, eta, gam, bet, W1, b1, W2, b2 = _mlp_problem(4, L, D, F)
+    out, st = _run_oracle_mlp(orc, q, k, v, 0 * eta, gam, bet, W1, b1, W2, b2, K=K)
+    T = torch.tensor
+    h = Fn.gelu(T(q @ W1 + b1), approximate="none").numpy() @ W2 + b2
+    ref = q + Fn.layer_norm(T(h), (D,), T(gam), T(bet), EPS).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+    assert math.isclose(np.abs(st[0] - W1).max(), 0.0)

@@ -1,0 +1,194 @@
+/*
+ * ttt.h -- C ABI of libttt, the MI355X (gfx950) hot path of TTT layers.
+ *
+ * A TTT layer keeps, per (batch, head), a hidden state that is itself a small
+ * model and trains it on the sequence while reading it: tokens are grouped in
+ * mini-batches of K; inside a mini-batch every token contributes the loss
+ *     l_j = 1/2 || LN(f(k_j)) - (v_j - k_j) ||^2
+ * at the mini-batch-start parameters, the output of token i is
+ *     out_i = q_i + LN(f_i(q_i)),
+ * where f_i is the state after one gradient step on the losses of tokens
+ * j <= i of the mini-batch, each weighted by the token's learning rate eta_j,
+ * and the step over the whole mini-batch is carried to the next one.
+ * TTT-Linear: f(x) = x W + b.  TTT-MLP: f(x) = GELU(x W1 + b1) W2 + b2.
+ *
+ * Sources (web pages, by title and listing/section):
+ *  - "代码连连看——TTT" (jiafeimiao.top): listings TTTBase.forward (layout,
+ *    rotary at position mod mini_batch_size, remainder handling),
+ *    TTTLinear.ttt (state tiling, dual/primal choice, cache update) and
+ *    compute_mini_batch (dual branch: Z1, Attn1, b1_bar, Z1_bar, W1_last,
+ *    b1_last; primal branch: grad_W1, W1_bar, the carried gradients);
+ *    closing remark that TTT-MLP is TTT-Linear stacked twice.
+ *  - "测试时学习（TTT）原理解析" (nanhubrain.csdn.net): TTTLinear parameter
+ *    init (section "TTT的核心创新"), TTTCache with seqlen_offset and
+ *    mini_batch_size (section "TTT缓存机制").
+ *  - ttt-lm-pytorch README (downcodes.com): TTT-Linear and TTT-MLP hidden
+ *    states; quick start with prefill and decoding.
+ *
+ * Readings where the pages leave a step open (the bodies of ln_fwd,
+ * ln_fused_l2_bwd, the rotary helpers, get_ttt_inputs and TTTCache.update are
+ * not printed):
+ *  - LN uses the population variance with eps inside the square root;
+ *    gamma/beta are per head ("ttt_norm_weight/bias" reshaped per head);
+ *  - the loss is half the squared error;
+ *  - eta_ij = token_eta_i * lr_j with token_eta = 1: one learning rate per
+ *    key token, the causal mask includes the diagonal;
+ *  - rotary embedding pairs dimension i with i + D/2, angle
+ *    p * base^(-2i/D), p = absolute position mod K; applied to q and k only,
+ *    before everything else (target and residual use the rotated values);
+ *  - between mini-batch boundaries the state holds the mini-batch-start W, b
+ *    plus the accumulated eta-weighted gradients (the pages' W1_grad,
+ *    b1_grad); they are committed and cleared at every boundary;
+ *  - TTT-MLP uses the exact (erf) GELU.
+ *
+ * Conventions for every entry point:
+ *  - Memory: the caller allocates every buffer (device memory unless stated)
+ *    and keeps ownership.  libttt allocates no device memory and keeps no
+ *    per-call state; its only global is the per-thread error message.
+ *  - Streams: ``stream`` is a hipStream_t passed as void* (NULL = the null
+ *    stream).  Calls only enqueue work; results are valid once the stream has
+ *    been synchronised.  There is no host/device synchronisation inside.
+ *  - Activations use ttt_tensor: element strides for batch, head and token,
+ *    the D values of one (b, h, t) contiguous.  The pages' [B, L, H*D] layout
+ *    is sB = L*H*D, sH = D, sL = H*D; [B, H, L, D] is sB = H*L*D, sH = L*D,
+ *    sL = D.  Data pointers and every stride in bytes must be multiples of
+ *    16 bytes.
+ *  - Errors: on any status other than TTT_OK nothing has been enqueued and
+ *    the state (including ``offset``) is unchanged.  ttt_last_error()
+ *    returns a per-thread message describing the last failure.
+ *  - NaN/Inf in the inputs propagate to the outputs; they are not checked.
+ *  - Calls on one state must be ordered (same stream, or synchronised);
+ *    calls on distinct states and buffers may run concurrently.
+ */
+#ifndef TTT_H
+#define TTT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ttt_status {
+    TTT_OK = 0,
+    TTT_ERR_NULL = 1,        /* a required pointer is NULL */
+    TTT_ERR_SHAPE = 2,       /* D != 64, K outside 1..16, B/H/L < 1, F != 256 */
+    TTT_ERR_DTYPE = 3,       /* unknown in/out dtype */
+    TTT_ERR_ALIGN = 4,       /* pointer or stride not a multiple of 16 bytes */
+    TTT_ERR_ALIAS = 5,       /* out overlaps an input or the state */
+    TTT_ERR_STATE = 6,       /* negative offset, or state incompatible with the call */
+    TTT_ERR_UNSUPPORTED = 7, /* valid request outside what is implemented */
+    TTT_ERR_HIP = 8          /* the HIP runtime reported an error at launch */
+} ttt_status;
+
+typedef enum ttt_dtype {
+    TTT_F32 = 0,
+    TTT_BF16 = 1
+} ttt_dtype;
+
+/* Strided activation tensor [B, H, L, D]; D contiguous; strides in elements. */
+typedef struct ttt_tensor {
+    void *data;
+    int64_t sB, sH, sL;
+} ttt_tensor;
+
+/* Learning rates eta[b, h, t] (fp32, token stride 1); sB = 0 shares them over
+ * the batch.  Row t of the block holds the rate of key token t
+ * ("ttt_lr_eta" in compute_mini_batch). */
+typedef struct ttt_eta {
+    const float *data;
+    int64_t sB, sH;
+} ttt_eta;
+
+typedef struct ttt_linear_cfg {
+    int32_t B, H;        /* batch, heads */
+    int32_t D;           /* head_dim, must be 64 */
+    int32_t K;           /* mini_batch_size, 1..16 (the MFMA dual-form path needs 16) */
+    int32_t in_dtype;    /* ttt_dtype of XQ, XK, XV */
+    int32_t out_dtype;   /* ttt_dtype of out */
+    int32_t rope;        /* 1: rotary embedding at position mod K on q and k */
+    float rope_base;     /* rotary base, e.g. 10000 */
+    float ln_eps;        /* LayerNorm eps, e.g. 1e-6 */
+} ttt_linear_cfg;
+
+/* TTTCache-style carried state of TTT-Linear (all fp32, device, contiguous):
+ *   W      [B, H, D, D]  mini-batch-start weights, row r = input dim
+ *   b      [B, H, D]     mini-batch-start bias
+ *   W_grad [B, H, D, D]  sum over the open mini-batch of eta_j k_j^T g_j
+ *   b_grad [B, H, D]     sum over the open mini-batch of eta_j g_j
+ *   offset (host)        tokens consumed so far (the cache's seqlen_offset);
+ *                        W_grad and b_grad are zero whenever offset % K == 0. */
+typedef struct ttt_linear_state {
+    float *W, *b, *W_grad, *b_grad;
+    int64_t offset;
+} ttt_linear_state;
+
+/* Initial state from the layer parameters ("TTTLinear.ttt": W1, b1 tiled over
+ * the batch, gradients zero).  W0 [H, D, D] and b0 [H, D] fp32 device,
+ * contiguous.  Sets offset = 0. */
+ttt_status ttt_linear_state_init(const ttt_linear_cfg *cfg, const float *W0, const float *b0,
+                                 ttt_linear_state *state, void *stream);
+
+/* Process L tokens of every (b, h) chain starting at state->offset.
+ * ("TTTBase.forward" + "TTTLinear.ttt" + "compute_mini_batch".)
+ *  XQ, XK, XV: [B, H, L, D] in cfg->in_dtype; eta as above (L per chain);
+ *  ln_w, ln_b: [H, D] fp32 device, contiguous (per-head LN gamma, beta);
+ *  out: [B, H, L, D] in cfg->out_dtype.
+ * Tokens that complete an open mini-batch and a trailing partial mini-batch
+ * run token by token (primal form); whole mini-batches run in the dual form
+ * on MFMA.  On success state->offset += L. */
+ttt_status ttt_linear_prefill(const ttt_linear_cfg *cfg, int32_t L, ttt_tensor XQ, ttt_tensor XK,
+                              ttt_tensor XV, ttt_eta eta, const float *ln_w, const float *ln_b,
+                              ttt_linear_state *state, ttt_tensor out, void *stream);
+
+/* Same function of (state, tokens) as ttt_linear_prefill, for a few tokens
+ * (typically T = 1): every token runs in the primal form ("compute_mini_batch",
+ * primal branch), the step is committed when a token closes a mini-batch.
+ * On success state->offset += T. */
+ttt_status ttt_linear_decode(const ttt_linear_cfg *cfg, int32_t T, ttt_tensor XQ, ttt_tensor XK,
+                             ttt_tensor XV, ttt_eta eta, const float *ln_w, const float *ln_b,
+                             ttt_linear_state *state, ttt_tensor out, void *stream);
+
+typedef struct ttt_mlp_cfg {
+    int32_t B, H;
+    int32_t D;           /* 64 */
+    int32_t F;           /* hidden width of the inner MLP, 256 */
+    int32_t K;           /* 16 */
+    int32_t in_dtype, out_dtype;
+    int32_t rope;
+    float rope_base;
+    float ln_eps;
+} ttt_mlp_cfg;
+
+/* Carried state of TTT-MLP (fp32, device, contiguous):
+ *   W1 [B, H, D, F], b1 [B, H, F], W2 [B, H, F, D], b2 [B, H, D],
+ *   W1_grad, b1_grad, W2_grad, b2_grad of the same shapes (open mini-batch),
+ *   offset (host). */
+typedef struct ttt_mlp_state {
+    float *W1, *b1, *W2, *b2;
+    float *W1_grad, *b1_grad, *W2_grad, *b2_grad;
+    int64_t offset;
+} ttt_mlp_state;
+
+/* W1 [H, D, F], b1 [H, F], W2 [H, F, D], b2 [H, D] fp32 device, contiguous.
+ * Tiles them over the batch, zeroes the gradients, sets offset = 0. */
+ttt_status ttt_mlp_state_init(const ttt_mlp_cfg *cfg, const float *W1, const float *b1, const float *W2,
+                              const float *b2, ttt_mlp_state *state, void *stream);
+
+/* TTT-MLP over L tokens in the dual form, whole mini-batches on MFMA.  Needs
+ * state->offset % K == 0 (TTT_ERR_UNSUPPORTED otherwise).  A trailing partial
+ * mini-batch of r < K tokens is computed with its outputs and left open: the
+ * parameters stay at the mini-batch start and the *_grad arrays receive its
+ * accumulated eta-weighted gradients.  On success state->offset += L. */
+ttt_status ttt_mlp_prefill(const ttt_mlp_cfg *cfg, int32_t L, ttt_tensor XQ, ttt_tensor XK, ttt_tensor XV,
+                           ttt_eta eta, const float *ln_w, const float *ln_b, ttt_mlp_state *state,
+                           ttt_tensor out, void *stream);
+
+const char *ttt_status_string(ttt_status s);
+const char *ttt_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTT_H */

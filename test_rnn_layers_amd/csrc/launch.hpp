@@ -1,0 +1,34 @@
+// launch.hpp -- host-side launchers of the libttt kernels (library-private).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "device_common.hpp"
+
+namespace ttt {
+
+// Everything a TTT-MLP launch needs (state [B*H, ...] fp32, F = 256).
+struct MlpArgs {
+    TDesc q, k, v;
+    const float *eta;
+    int64_t eta_sB, eta_sH;
+    const float *ln_w, *ln_b;
+    float *W1, *b1, *W2, *b2;
+    float *W1g, *b1g, *W2g, *b2g;
+    ODesc out;
+    int32_t B, H;
+    int32_t nblk;     // mini-batches, the last one possibly partial
+    int32_t tail;     // tokens in the last mini-batch if partial, else 0
+    int32_t t0;
+    int64_t pos0;
+    int32_t rope;
+    float rope_base;
+    float eps;
+};
+
+hipError_t launch_linear_token(const LinearArgs &a, int in_bf16, int out_bf16, hipStream_t s);
+hipError_t launch_linear_dual(const LinearArgs &a, int in_bf16, int out_bf16, hipStream_t s);
+hipError_t launch_mlp_dual(const MlpArgs &a, int in_bf16, int out_bf16, hipStream_t s);
+hipError_t launch_tile(float *dst, const float *src, int64_t per, int64_t total, hipStream_t s);
+
+}  // namespace ttt

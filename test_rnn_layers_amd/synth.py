@@ -71,21 +71,21 @@ def make_inputs(B: int, H: int, L: int, *, D: int = D_HEAD, dtype: str = "f32", 
         F = mlp_hidden
         out["W1"] = torch.randn((H, D, F), generator=g, dtype=torch.float32) * 0.02
         out["W2"] = torch.randn((H, F, D), generator=g, dtype=torch.float32) * 0.02
-        out["b1"] = torch.zeros((H, F))
-        out["b2"] = torch.zeros((H, D))
+        out["b1"] = torch.zeros((H, F), dtype=torch.float32)
+        out["b2"] = torch.zeros((H, D), dtype=torch.float32)
     else:
         out["W0"] = torch.randn((H, D, D), generator=g, dtype=torch.float32) * 0.02
-        out["b0"] = torch.zeros((H, D))
-    out["ln_w"] = torch.ones((H, D))
-    out["ln_b"] = torch.zeros((H, D))
+        out["b0"] = torch.zeros((H, D), dtype=torch.float32)
+    out["ln_w"] = torch.ones((H, D), dtype=torch.float32)
+    out["ln_b"] = torch.zeros((H, D), dtype=torch.float32)
     if rich:
-        out["ln_w"] = 1.0 + 0.2 * torch.randn((H, D), generator=g)
-        out["ln_b"] = 0.2 * torch.randn((H, D), generator=g)
+        out["ln_w"] = 1.0 + 0.2 * torch.randn((H, D), generator=g, dtype=torch.float32)
+        out["ln_b"] = 0.2 * torch.randn((H, D), generator=g, dtype=torch.float32)
         if mlp_hidden:
-            out["b1"] = 0.05 * torch.randn((H, mlp_hidden), generator=g)
-            out["b2"] = 0.05 * torch.randn((H, D), generator=g)
+            out["b1"] = 0.05 * torch.randn((H, mlp_hidden), generator=g, dtype=torch.float32)
+            out["b2"] = 0.05 * torch.randn((H, D), generator=g, dtype=torch.float32)
         else:
-            out["b0"] = 0.05 * torch.randn((H, D), generator=g)
+            out["b0"] = 0.05 * torch.randn((H, D), generator=g, dtype=torch.float32)
     return out
 
 

@@ -1,0 +1,97 @@
+"""Shared helpers of the parity tests: run the HIP path through the C ABI and
+the CPU oracle on the same seeded inputs."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from test_rnn_layers_amd import libttt
+from test_rnn_layers_amd.synth import make_inputs
+
+TOL_F32 = 1e-4   # max-abs error, fp32 inputs
+TOL_BF16 = 2e-2  # max-abs error, bf16 inputs, fp32 state
+
+
+def tol_for(dtype: str) -> float:
+    return TOL_F32 if dtype == "f32" else TOL_BF16
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+class LinearGPU:
+    """One TTT-Linear problem on the GPU: device inputs, state, out."""
+
+    def __init__(self, inp: dict, *, K=16, rope=False, in_dtype="bf16", out_dtype="f32", layout="bhld",
+                 device="cuda"):
+        self.inp = inp
+        B, H, L, D = inp["XQ"].shape
+        self.B, self.H, self.L, self.D = B, H, L, D
+        self.cfg = libttt.linear_cfg(B, H, K=K, in_dtype=in_dtype, out_dtype=out_dtype, rope=rope)
+        self.K, self.rope, self.out_dtype = K, rope, out_dtype
+        self.layout = layout
+        self.x = {n: self._place(inp[n].to(device)) for n in ("XQ", "XK", "XV")}
+        self.eta = inp["eta"].to(device)
+        self.ln_w, self.ln_b = inp["ln_w"].to(device).contiguous(), inp["ln_b"].to(device).contiguous()
+        self.W0, self.b0 = inp["W0"].to(device).contiguous(), inp["b0"].to(device).contiguous()
+        odt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+        self.out = self._place(torch.full((B, H, L, D), float("nan"), dtype=odt, device=device))
+        self.state = libttt.LinearState.empty(B, H, D, device=device)
+        libttt.ttt_linear_state_init(self.cfg, self.W0, self.b0, self.state)
+
+    def _place(self, t):
+        """[B, H, L, D] contiguous -> the requested memory layout (same values)."""
+        if self.layout == "bhld":
+            return t.contiguous()
+        # the pages' [B, L, H*D] projection output viewed as [B, H, L, D]
+        B, H, L, D = t.shape
+        return t.permute(0, 2, 1, 3).contiguous().view(B, L, H, D).permute(0, 2, 1, 3)
+
+    def run(self, t0, t1, decode=False):
+        """Tokens [t0, t1) in one prefill (or decode) call."""
+        sl = slice(t0, t1)
+        fn = libttt.ttt_linear_decode if decode else libttt.ttt_linear_prefill
+        fn(self.cfg, t1 - t0, self.x["XQ"][:, :, sl], self.x["XK"][:, :, sl], self.x["XV"][:, :, sl],
+           self.eta[:, sl], self.ln_w, self.ln_b, self.state, self.out[:, :, sl])
+
+    def result(self):
+        torch.cuda.synchronize()
+        s = self.state
+        return (to_f64(self.out), to_f64(s.W), to_f64(s.b), to_f64(s.W_grad), to_f64(s.b_grad))
+
+
+def oracle_linear(inp: dict, *, K=16, rope=False, chains=None, L=None):
+    """Oracle outputs and final state for the listed (b, h) chains (default all).
+    Returns out [n, L, D], W, b, G, gb per chain."""
+    B, H, Lf, D = inp["XQ"].shape
+    L = Lf if L is None else L
+    chains = [(b, h) for b in range(B) for h in range(H)] if chains is None else chains
+    outs, Ws, bs, Gs, gbs = [], [], [], [], []
+    eta, lw, lb = to_f64(inp["eta"]), to_f64(inp["ln_w"]), to_f64(inp["ln_b"])
+    W0, b0 = to_f64(inp["W0"]), to_f64(inp["b0"])
+    for (b, h) in chains:
+        q, k, v = (to_f64(inp[n][b, h, :L]) for n in ("XQ", "XK", "XV"))
+        W, bb, G, gb = W0[h].copy(), b0[h].copy(), np.zeros((D, D)), np.zeros(D)
+        o = oracle.linear_chain(q, k, v, eta[h, :L], lw[h], lb[h], W, bb, G, gb, K=K, rope=rope)
+        outs.append(o)
+        Ws.append(W)
+        bs.append(bb)
+        Gs.append(G)
+        gbs.append(gb)
+    return np.stack(outs), np.stack(Ws), np.stack(bs), np.stack(Gs), np.stack(gbs)
+
+
+def max_abs(a, b) -> float:
+    return float(np.max(np.abs(np.asarray(a) - np.asarray(b))))
+
+
+def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
+    """Half a bf16 ulp of |x| (the rounding bound of a bf16 store)."""
+    ax = np.maximum(np.abs(x), np.finfo(np.float32).tiny)
+    return np.exp2(np.floor(np.log2(ax)) - 8)
+
+
+__all__ = ["LinearGPU", "oracle_linear", "max_abs", "tol_for", "make_inputs", "to_f64", "bf16_half_ulp",
+           "TOL_F32", "TOL_BF16"]

@@ -1,0 +1,129 @@
+"""libttt loads, exports every function include/ttt.h declares, and rejects bad
+arguments with the documented status before touching the GPU.  The error
+paths return before any HIP call, so these run without a GPU (the pointers
+below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from test_rnn_layers_amd import libttt as T
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ttt.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const char \*|ttt_status )\s*(ttt_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert set(_declared()) == set(T.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = T.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code, name in T.STATUS_NAMES.items():
+        assert T.ttt_status_string(code) == name
+
+
+# fake, 16-byte aligned, non-overlapping device addresses (never dereferenced)
+B, H, L, D = 2, 3, 40, 64
+MB = 1 << 20
+BASE = 0x7F0000000000
+
+
+def _addr(i):
+    return BASE + i * 64 * MB
+
+
+def _args(**over):
+    es = 2
+    a = dict(
+        cfg=T.linear_cfg(B, H, in_dtype="bf16", out_dtype="f32"),
+        L=L,
+        XQ=T.ttt_tensor(_addr(0), H * L * D, L * D, D),
+        XK=T.ttt_tensor(_addr(1), H * L * D, L * D, D),
+        XV=T.ttt_tensor(_addr(2), H * L * D, L * D, D),
+        eta=T.ttt_eta(_addr(3), 0, L),
+        ln_w=_addr(4),
+        ln_b=_addr(5),
+        state=T.ttt_linear_state(_addr(6), _addr(7), _addr(8), _addr(9), 0),
+        out=T.ttt_tensor(_addr(10), H * L * D, L * D, D),
+    )
+    del es
+    a.update(over)
+    return a
+
+
+def _call(fn="ttt_linear_prefill", **over):
+    a = _args(**over)
+    lib = T.load()
+    cfg = ctypes.byref(a["cfg"]) if a["cfg"] is not None else None
+    st = ctypes.byref(a["state"]) if a["state"] is not None else None
+    rc = getattr(lib, fn)(cfg, a["L"], a["XQ"], a["XK"], a["XV"], a["eta"], a["ln_w"], a["ln_b"], st, a["out"],
+                          None)
+    return rc, a
+
+
+def _cfg(**kw):
+    c = T.linear_cfg(B, H, in_dtype="bf16", out_dtype="f32")
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+CASES = [
+    ("null cfg", dict(cfg=None), "TTT_ERR_NULL"),
+    ("null XQ", dict(XQ=T.ttt_tensor(None, H * L * D, L * D, D)), "TTT_ERR_NULL"),
+    ("null eta", dict(eta=T.ttt_eta(None, 0, L)), "TTT_ERR_NULL"),
+    ("null ln", dict(ln_w=None), "TTT_ERR_NULL"),
+    ("null state", dict(state=None), "TTT_ERR_NULL"),
+    ("null W_grad", dict(state=T.ttt_linear_state(_addr(6), _addr(7), None, _addr(9), 0)), "TTT_ERR_NULL"),
+    ("D=32", dict(cfg=_cfg(D=32)), "TTT_ERR_SHAPE"),
+    ("K=0", dict(cfg=_cfg(K=0)), "TTT_ERR_SHAPE"),
+    ("K=17", dict(cfg=_cfg(K=17)), "TTT_ERR_SHAPE"),
+    ("B=0", dict(cfg=_cfg(B=0)), "TTT_ERR_SHAPE"),
+    ("L=0", dict(L=0), "TTT_ERR_SHAPE"),
+    ("eps=0", dict(cfg=_cfg(ln_eps=0.0)), "TTT_ERR_SHAPE"),
+    ("dtype", dict(cfg=_cfg(in_dtype=7)), "TTT_ERR_DTYPE"),
+    ("misaligned XK", dict(XK=T.ttt_tensor(_addr(1) + 8, H * L * D, L * D, D)), "TTT_ERR_ALIGN"),
+    ("odd token stride", dict(XV=T.ttt_tensor(_addr(2), H * L * 68, L * 68, 68 + 2)), "TTT_ERR_ALIGN"),
+    ("negative stride", dict(XQ=T.ttt_tensor(_addr(0), H * L * D, L * D, -D)), "TTT_ERR_ALIGN"),
+    ("misaligned state", dict(state=T.ttt_linear_state(_addr(6) + 4, _addr(7), _addr(8), _addr(9), 0)),
+     "TTT_ERR_ALIGN"),
+    ("out overlaps XQ", dict(out=T.ttt_tensor(_addr(0) + 4096, H * L * D, L * D, D)), "TTT_ERR_ALIAS"),
+    ("out overlaps state", dict(out=T.ttt_tensor(_addr(8), H * L * D, L * D, D)), "TTT_ERR_ALIAS"),
+    ("out rows overlap", dict(out=T.ttt_tensor(_addr(10), H * L * D, L * D, 32)), "TTT_ERR_ALIAS"),
+    ("state buffers overlap", dict(state=T.ttt_linear_state(_addr(6), _addr(6) + 64, _addr(8), _addr(9), 0)),
+     "TTT_ERR_ALIAS"),
+    ("negative offset", dict(state=T.ttt_linear_state(_addr(6), _addr(7), _addr(8), _addr(9), -3)),
+     "TTT_ERR_STATE"),
+]
+
+
+@pytest.mark.parametrize("fn", ["ttt_linear_prefill", "ttt_linear_decode"])
+@pytest.mark.parametrize("label,over,expect", CASES, ids=[c[0] for c in CASES])
+def test_error_paths(fn, label, over, expect):
+    rc, a = _call(fn, **over)
+    assert T.STATUS_NAMES[rc] == expect, (label, T.ttt_last_error())
+    assert T.ttt_last_error(), "a failed call leaves a message"
+    if a["state"] is not None:
+        assert a["state"].offset == over.get("state", a["state"]).offset  # unchanged on error
+
+
+def test_state_init_errors():
+    lib = T.load()
+    st = T.ttt_linear_state(_addr(6), _addr(7), _addr(8), _addr(9), 5)
+    assert T.STATUS_NAMES[lib.ttt_linear_state_init(ctypes.byref(_cfg()), None, _addr(4), ctypes.byref(st), None)] \
+        == "TTT_ERR_NULL"
+    assert T.STATUS_NAMES[lib.ttt_linear_state_init(ctypes.byref(_cfg(D=16)), _addr(1), _addr(4), ctypes.byref(st),
+                                                    None)] == "TTT_ERR_SHAPE"
+    assert st.offset == 5

@@ -1,0 +1,171 @@
+"""GPU parity of TTT-Linear (prefill, decode, head/tail pieces) against the
+CPU oracle, through the C ABI.  Tolerances: max-abs 1e-4 for fp32 inputs,
+2e-2 for bf16 inputs with the fp32 state."""
+import numpy as np
+import pytest
+import torch
+
+from harness import (LinearGPU, bf16_half_ulp, make_inputs, max_abs, oracle_linear, tol_for)
+from test_rnn_layers_amd.synth import WORKLOADS, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _report(name, **kv):
+    print(f"[{name}] " + " ".join(f"{k}={v:.3e}" if isinstance(v, float) else f"{k}={v}" for k, v in kv.items()),
+          flush=True)
+
+
+def _check_full(name, inp, *, dtype, rope=False, K=16, pieces=None, layout="bhld", out_dtype="f32", decode=()):
+    """Run the GPU on [0, L) split at `pieces` (list of cut points), compare
+    every output and the final state with the oracle."""
+    B, H, L, D = inp["XQ"].shape
+    g = LinearGPU(inp, K=K, rope=rope, in_dtype=dtype, out_dtype=out_dtype, layout=layout)
+    cuts = [0] + list(pieces or []) + [L]
+    for i in range(len(cuts) - 1):
+        g.run(cuts[i], cuts[i + 1], decode=cuts[i] in decode)
+    out, W, b, G, gb = g.result()
+    ro, rW, rb, rG, rgb = oracle_linear(inp, K=K, rope=rope)
+    out = out.reshape(B * H, L, D)
+    err = max_abs(out, ro)
+    tol = tol_for(dtype)
+    if out_dtype == "bf16":
+        excess = np.max(np.abs(out - ro) - bf16_half_ulp(ro))
+        _report(name, err=err, excess_over_bf16_rounding=float(excess))
+        assert excess <= tol
+    else:
+        _report(name, err=err, W=max_abs(W.reshape(rW.shape), rW), b=max_abs(b.reshape(rb.shape), rb))
+        assert err <= tol, f"{name}: max-abs {err} > {tol}"
+    assert np.isfinite(out).all()
+    sc = max(1.0, float(np.abs(rW).max()))
+    assert max_abs(W.reshape(rW.shape), rW) <= tol * sc
+    assert max_abs(b.reshape(rb.shape), rb) <= tol * sc
+    assert max_abs(G.reshape(rG.shape), rG) <= tol * sc
+    assert max_abs(gb.reshape(rgb.shape), rgb) <= tol * sc
+    return out, ro
+
+
+def test_single_head_f32_workload():
+    w = WORKLOADS[0]
+    _check_full(w.name, workload_inputs(w), dtype="f32")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rope", [False, True])
+def test_small_rich_parity(dtype, rope):
+    """Several chains, non-trivial b0/gamma/beta, ragged tail (L = 5*16 + 7)."""
+    inp = make_inputs(2, 3, 87, dtype=dtype, seed=11 + rope, rich=True)
+    _check_full(f"small_{dtype}_rope{int(rope)}", inp, dtype=dtype, rope=rope)
+
+
+def test_strided_projection_layout():
+    """Inputs and output in the pages' [B, L, H*D] layout (strided views)."""
+    inp = make_inputs(2, 4, 64, dtype="bf16", seed=5, rich=True)
+    _check_full("layout_blhd", inp, dtype="bf16", layout="blhd")
+
+
+@pytest.mark.parametrize("cuts", [[5], [16, 21], [3, 40, 41, 57], [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15]])
+def test_pieces_with_open_minibatches(cuts):
+    """Calls that start and end inside mini-batches (head, body and tail)."""
+    inp = make_inputs(2, 2, 70, dtype="f32", seed=23, rich=True)
+    _check_full(f"pieces_{cuts}", inp, dtype="f32", pieces=cuts)
+
+
+@pytest.mark.parametrize("K", [1, 4, 13])
+def test_other_minibatch_sizes(K):
+    inp = make_inputs(1, 3, 40, dtype="f32", seed=31 + K, rich=True)
+    _check_full(f"K{K}", inp, dtype="f32", K=K, pieces=[7])
+
+
+def test_decode_steps_f32():
+    inp = make_inputs(2, 2, 48, dtype="f32", seed=3, rich=True)
+    cuts = [20] + list(range(21, 48))
+    _check_full("decode_f32", inp, dtype="f32", pieces=cuts, decode=set(cuts))
+
+
+def test_bf16_output():
+    inp = make_inputs(2, 2, 64, dtype="bf16", seed=8)
+    _check_full("bf16_out", inp, dtype="bf16", out_dtype="bf16")
+
+
+def test_deterministic():
+    inp = make_inputs(2, 4, 96, dtype="bf16", seed=9, rich=True)
+    outs = []
+    for _ in range(2):
+        g = LinearGPU(inp, in_dtype="bf16")
+        g.run(0, 96)
+        outs.append(g.result())
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b, equal_nan=True)
+
+
+def test_eta_zero_leaves_state():
+    inp = make_inputs(1, 2, 48, dtype="f32", seed=4, rich=True)
+    inp["eta"] = torch.zeros_like(inp["eta"])
+    out, ro = _check_full("eta0", inp, dtype="f32")
+    g = LinearGPU(inp, in_dtype="f32")
+    g.run(0, 48)
+    _, W, b, _, _ = g.result()
+    assert np.array_equal(W[0], inp["W0"].double().numpy())
+
+
+def test_minimum_inputs():
+    """B = H = 1 and a single token."""
+    inp = make_inputs(1, 1, 1, dtype="bf16", seed=2)
+    _check_full("one_token", inp, dtype="bf16")
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads: every output is produced, sampled chains are compared
+# with the oracle, all outputs checked finite
+# ---------------------------------------------------------------------------
+def _full_size(w, chains, *, rope):
+    inp = workload_inputs(w)
+    B, H, L, D = inp["XQ"].shape
+    g = LinearGPU(inp, rope=rope, in_dtype=w.dtype)
+    g.run(0, L)
+    out, W, b, _, _ = g.result()
+    assert np.isfinite(out).all()
+    ro, rW, rb, _, _ = oracle_linear(inp, rope=rope, chains=chains)
+    errs = []
+    for i, (bb, h) in enumerate(chains):
+        errs.append(max_abs(out[bb, h], ro[i]))
+        assert max_abs(W[bb, h], rW[i]) <= tol_for(w.dtype) * max(1.0, np.abs(rW[i]).max())
+    # error per mini-batch index, to see drift along the chain
+    e_blocks = np.abs(out[chains[0][0], chains[0][1]] - ro[0]).reshape(-1, 16 * D).max(axis=1)
+    _report(w.name, err=max(errs), first_blocks=float(e_blocks[:8].max()), last_blocks=float(e_blocks[-8:].max()))
+    assert max(errs) <= tol_for(w.dtype)
+
+
+def test_full_125m_rope_workload():
+    w = WORKLOADS[1]
+    _full_size(w, [(0, 0), (3, 7), (7, 11)], rope=True)
+
+
+def test_full_1b_workload():
+    w = WORKLOADS[2]
+    _full_size(w, [(0, 0), (2, 17), (3, 31)], rope=False)
+
+
+def test_decode_workload():
+    """Prefill 512 tokens, then 256 single-token decode calls; compared with
+    the oracle on sampled chains and with one GPU prefill over all 768."""
+    w = WORKLOADS[4]
+    inp = workload_inputs(w)
+    B, H, L, D = inp["XQ"].shape
+    g = LinearGPU(inp, in_dtype="bf16")
+    g.run(0, w.prefill)
+    for t in range(w.prefill, L):
+        g.run(t, t + 1, decode=True)
+    out, W, b, G, gb = g.result()
+    assert g.state.offset == L
+    whole = LinearGPU(inp, in_dtype="bf16")
+    whole.run(0, L)
+    out2, W2, _, _, _ = whole.result()
+    chains = [(0, 0), (17, 5), (40, 31), (63, 12)]
+    ro, rW, _, rG, _ = oracle_linear(inp, chains=chains)
+    errs = [max_abs(out[bb, h], ro[i]) for i, (bb, h) in enumerate(chains)]
+    _report(w.name, err=max(errs), gpu_split_vs_whole=max_abs(out, out2))
+    assert max(errs) <= tol_for("bf16")
+    assert max_abs(out, out2) <= tol_for("bf16")
+    assert max_abs(W, W2) <= 1e-3 * max(1.0, np.abs(W2).max())

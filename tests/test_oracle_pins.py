@@ -25,7 +25,7 @@ import pytest
 import torch
 import torch.nn.functional as Fn
 
-torch.set_default_dtype(torch.float64)
+
 EPS = 1e-6
 
 

@@ -11,22 +11,25 @@
 //   out_n  = Q_n + LN(Zbar_n)
 //   W_n+1  = W_n + K_n^T ng_n ,  b_n+1 = b_n + 1^T ng_n   (W1_last, b1_last)
 //
-// Design (gfx950, one persistent workgroup of 4 waves per (batch, head)):
-//  * Wave w owns the 64x16 column slab W[:, 16w..16w+15] as four MFMA
-//    accumulator tiles (fp32) for the whole chain, and b as a fifth tile whose
-//    rows all hold b.  Every product keeps that slab as its B operand.
-//  * Look-ahead: Z_n+1 = K_n+1 W_n + b_n + (K_n+1 K_n^T + 1) ng_n.  The first
-//    term (Y_n+1) is formed while mini-batch n is still in flight, so the
-//    sequential chain per mini-batch is one 16x16x16 product, a LayerNorm
-//    backward and two barriers.
-//  * Row-wise LayerNorm work: 16 lanes per row, 4 columns per lane, row sums
-//    with DPP butterflies; results cross between the row and the column
-//    layouts through LDS (Z, Zbar out; ng back as MFMA B fragments).
-//  * Operands: bf16 inputs run the products on fp16 MFMA (inputs, the W slab,
-//    ng and the 16x16 matrices rounded to fp16, fp32 accumulation; ~2^-11
-//    relative per operand); fp32 inputs run them on fp32 MFMA.
-//  * Inputs stream through a 4-deep LDS ring; each thread fetches its share
-//    of a mini-batch 3 mini-batches ahead into registers.
+// Design (gfx950, one persistent workgroup of 8 waves per (batch, head)):
+//  * Column waves 0..3: wave c owns the 64x16 slab W[:, 16c..16c+15] as four
+//    fp32 MFMA accumulator tiles for the whole chain (and b as a tile whose
+//    rows all hold b) and runs every product of the step.
+//  * Row waves 4..7: 16 lanes per token row, 4 columns per lane.  They fetch
+//    the inputs of mini-batch n+6, stage n+2 into LDS as MFMA row fragments,
+//    keep the LayerNorm target and the residual in registers, and run the
+//    LayerNorm backward (-> ng, to LDS as MFMA B fragments) and forward
+//    (-> out, stored to HBM) with DPP row reductions.
+//  * Look-ahead on the sequential chain:
+//      Z_n+1 = K_n+1 W_n + b_n + (K_n+1 K_n^T + 1) ng_n,
+//    the first term formed while ng_n is being computed, so each mini-batch
+//    costs one 16x16x16 product, one LayerNorm backward and two barriers on
+//    the critical path.  The two wave roles share each SIMD and overlap.
+//  * K^T fragments for the state step come from an MFMA of K against a 0/1
+//    selection pattern (exact), instead of a transposed copy in LDS.
+//  * Operands: bf16 inputs run the products on fp16 MFMA (inputs, W, ng and
+//    the 16x16 matrices rounded to fp16; fp32 accumulation); fp32 inputs run
+//    them on fp32 MFMA.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -36,9 +39,8 @@ namespace ttt {
 namespace {
 
 constexpr int kM = 16;     // mini-batch size of this kernel
-constexpr int kRing = 4;   // LDS stages: n-1, n, n+1, n+2
-constexpr int kAhead = 3;  // register prefetch depth (mini-batches)
-constexpr int kFP = 68;    // fp32 row pitch (16 B aligned, skews banks)
+constexpr int kRing = 4;   // LDS stages and register sets (mini-batch mod 4)
+constexpr int kFP = 68;    // fp32 row pitch of the exchange buffers
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -49,18 +51,29 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 template <typename T>
 struct Op;
 
-// fp16 operands: 16x16x32 (k = 64 products, two steps) and 16x16x16 MFMAs.
+// fp16 operands: 16x16x32 MFMAs for the k = 64 products (two steps),
+// 16x16x16 for the k = 16 ones.  Lane (g, n): A row n, B column n, k slots
+// 8g..8g+7 (resp. 4g..4g+3); C rows 4g..4g+3, column n.
 template <>
 struct Op<_Float16> {
     static constexpr int XP = 72;  // row pitch of X tiles (144 B)
-    static constexpr int TP = 24;  // token pitch of the transposed K tile
+    static constexpr int GP = 68;  // row pitch of the ng tile: rows 4 apart land 8 banks apart
     using F4 = h4;
     struct XF {
         h8 v[2];
     };
-    using WF = XF;
-    // Row n of a 16x64 tile with the k permutation matching the accumulator
-    // layout of W: slot 8g+i <- column 32s + 4g + i (i < 4), 32s + 16 + 4g + i-4.
+    // B fragment of a row-major [token][column] tile: tokens 4g..4g+3 of column col
+    __device__ static F4 load_b(const _Float16 *G, int col, int g) {
+        return F4{G[(4 * g) * GP + col], G[(4 * g + 1) * GP + col], G[(4 * g + 2) * GP + col],
+                  G[(4 * g + 3) * GP + col]};
+    }
+    // selection patterns for K^T: element i of pattern h is 1 where slot
+    // 8g+i carries column 16r + n of the output tile (r = 2s + h)
+    struct Sel {
+        h8 p[2];
+    };
+    // Row n of a 16x64 tile, k permuted to match the accumulator layout of W:
+    // slot 8g+i <- column 32s + 4g + i (i < 4), 32s + 16 + 4g + i - 4 (i >= 4).
     __device__ static XF load_x(const _Float16 *X, int n, int g) {
         XF x;
 #pragma unroll
@@ -71,8 +84,8 @@ struct Op<_Float16> {
         }
         return x;
     }
-    __device__ static WF cvt_w(const f32x4 (&Wt)[4]) {
-        WF w;
+    __device__ static XF cvt_w(const f32x4 (&Wt)[4]) {
+        XF w;
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -90,34 +103,54 @@ struct Op<_Float16> {
     __device__ static f32x4 mma16(F4 a, F4 b, f32x4 acc) {
         return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, acc, 0, 0, 0);
     }
-    __device__ static F4 make(float x0, float x1, float x2, float x3) {
-        return F4{(_Float16)x0, (_Float16)x1, (_Float16)x2, (_Float16)x3};
+    __device__ static F4 make(f32x4 x) { return F4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]}; }
+    __device__ static Sel sel(int n, int g) {
+        Sel s;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                s.p[h][i] = (i / 4 == h && 4 * g + (i & 3) == n) ? (_Float16)1.f : (_Float16)0.f;
+        return s;
+    }
+    // tile r of K (rows = tokens, columns 16r..16r+15) in accumulator layout,
+    // i.e. the A fragment of K^T rows 16r..16r+15: lane holds K[4g+j][16r+n]
+    __device__ static void kt_frags(const XF &k, const Sel &s, F4 (&kt)[4]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            kt[r] = make(__builtin_amdgcn_mfma_f32_16x16x32_f16(k.v[r >> 1], s.p[r & 1], f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                 0, 0, 0));
+    }
+    __device__ static void put4(_Float16 *p, float x0, float x1, float x2, float x3) {
+        *(h4 *)p = h4{(_Float16)x0, (_Float16)x1, (_Float16)x2, (_Float16)x3};
     }
     __device__ static void put(_Float16 *p, float x) { *p = (_Float16)x; }
-    __device__ static void put2(_Float16 *p, float x0, float x1) {
-        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-        *(h2 *)p = h2{(_Float16)x0, (_Float16)x1};
-    }
 };
 
 // fp32 operands: 16x16x4 fp32 MFMAs (A lane (g,n) holds A[n][g], B holds B[g][n]).
 template <>
 struct Op<float> {
     static constexpr int XP = 68;
-    static constexpr int TP = 20;
+    static constexpr int GP = 68;
     using F4 = f32x4;
     struct XF {
         f32x4 v[4];  // v[r][j] = X[n][16r + 4g + j]
     };
-    using WF = XF;
+    __device__ static F4 load_b(const float *G, int col, int g) {
+        return F4{G[(4 * g) * GP + col], G[(4 * g + 1) * GP + col], G[(4 * g + 2) * GP + col],
+                  G[(4 * g + 3) * GP + col]};
+    }
+    struct Sel {
+        float p[4];  // p[j] = 1 where 4g + j == n
+    };
     __device__ static XF load_x(const float *X, int n, int g) {
         XF x;
 #pragma unroll
         for (int r = 0; r < 4; ++r) x.v[r] = *(const f32x4 *)(X + n * XP + 16 * r + 4 * g);
         return x;
     }
-    __device__ static WF cvt_w(const f32x4 (&Wt)[4]) {
-        WF w;
+    __device__ static XF cvt_w(const f32x4 (&Wt)[4]) {
+        XF w;
 #pragma unroll
         for (int r = 0; r < 4; ++r) w.v[r] = Wt[r];
         return w;
@@ -136,9 +169,26 @@ struct Op<float> {
         for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], acc, 0, 0, 0);
         return acc;
     }
-    __device__ static F4 make(float x0, float x1, float x2, float x3) { return F4{x0, x1, x2, x3}; }
+    __device__ static F4 make(f32x4 x) { return x; }
+    __device__ static Sel sel(int n, int g) {
+        Sel s;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s.p[j] = (4 * g + j == n) ? 1.f : 0.f;
+        return s;
+    }
+    __device__ static void kt_frags(const XF &k, const Sel &s, F4 (&kt)[4]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k.v[r][j], s.p[j], acc, 0, 0, 0);
+            kt[r] = acc;
+        }
+    }
+    __device__ static void put4(float *p, float x0, float x1, float x2, float x3) {
+        *(f32x4 *)p = f32x4{x0, x1, x2, x3};
+    }
     __device__ static void put(float *p, float x) { *p = x; }
-    __device__ static void put2(float *p, float x0, float x1) { *(float2 *)p = float2{x0, x1}; }
 };
 
 // ---------------------------------------------------------------------------
@@ -146,31 +196,26 @@ struct Op<float> {
 // ---------------------------------------------------------------------------
 template <typename T>
 struct Stage {
-    T kx[kM][Op<T>::XP];        // K rows (rotated), operand type
-    T qx[kM][Op<T>::XP];        // Q rows (rotated)
-    T kt[kD][Op<T>::TP];        // K transposed: kt[d][token]
-    float cel[kM][kFP];         // gamma * (beta - v + k), per element
-    float qres[kM][kFP];        // q + beta
-    float eta[kM];
+    T kx[kM][Op<T>::XP];  // K rows (rotated), operand type
+    T qx[kM][Op<T>::XP];  // Q rows (rotated)
 };
 
 template <typename T>
 struct Smem {
     Stage<T> st[kRing];
-    float zbuf[kM][kFP];                 // Z_n (column layout in, row layout out)
-    float zbbuf[kM][kFP];                // Zbar_n-1
-    typename Op<T>::F4 gop[kD][4];       // ng as B fragments: [column][token group]
-    typename Op<T>::F4 mop[64];          // tril(Q K^T + 1) as A fragments, per lane
-    typename Op<T>::F4 cop[64];          // K_n+1 K_n^T + 1 as A fragments, per lane
+    float zbuf[kM][kFP];            // Z_n: written by column waves, read by row waves
+    float zbbuf[2][kM][kFP];        // Zbar_n, double-buffered (read two steps later)
+    T gm[kM][Op<T>::GP];            // ng, row-major [token][column]
 };
 
 // ---------------------------------------------------------------------------
-// row reductions over the 16 lanes of a DPP row (all lanes get the sum)
+// DPP within a row of 16 lanes
 // ---------------------------------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
+// sum over the 16 lanes of the row; every lane receives it
 __device__ __forceinline__ float row_sum16(float x) {
     x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
     x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
@@ -178,104 +223,276 @@ __device__ __forceinline__ float row_sum16(float x) {
     x += dpp<0x140>(x);  // row_mirror
     return x;
 }
+// value of lane (n + 8) mod 16 of the row (the lane holding columns +-32)
+__device__ __forceinline__ float row_swap8(float x) { return dpp<0x128>(x); }  // row_ror:8
 
 // ---------------------------------------------------------------------------
-// per-thread share of one mini-batch's inputs: row tid/16, columns
-// c0 = 2*(tid%16), c0+1 and c0+32, c0+33 of each of q, k, v
+// row waves: inputs of one mini-batch for token row t, columns 4n .. 4n+3
 // ---------------------------------------------------------------------------
-template <typename Tin>
-struct Pref;
-template <>
-struct Pref<__bf16> {
-    uint32_t q[2], k[2], v[2];  // two bf16 each
-    float eta;
-    __device__ static void unpack(uint32_t u, float &a, float &b) {
-        a = __builtin_bit_cast(float, u << 16);
-        b = __builtin_bit_cast(float, u & 0xffff0000u);
-    }
-};
-template <>
-struct Pref<float> {
-    float2 q[2], k[2], v[2];
-    float eta;
-    __device__ static void unpack(float2 u, float &a, float &b) {
-        a = u.x;
-        b = u.y;
-    }
-};
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t Rsrc;
 
-template <typename Tin>
-struct InPtr {
-    const Tin *q, *k, *v;  // at (b, h, token t0, column c0) of this thread
-    const float *eta;      // at (b, h, token t0)
-    int64_t sq, sk, sv;    // token strides
-};
-
-template <typename Tin>
-__device__ __forceinline__ void fetch(Pref<Tin> &p, const InPtr<Tin> &ip, int blk, int row, int tid) {
-    using U = decltype(p.q[0]);
-    using UU = typename std::remove_reference<U>::type;
-    const int64_t t = (int64_t)blk * kM + row;
-    const Tin *q = ip.q + t * ip.sq, *k = ip.k + t * ip.sk, *v = ip.v + t * ip.sv;
-    p.q[0] = *(const UU *)q;
-    p.q[1] = *(const UU *)(q + 32);
-    p.k[0] = *(const UU *)k;
-    p.k[1] = *(const UU *)(k + 32);
-    p.v[0] = *(const UU *)v;
-    p.v[1] = *(const UU *)(v + 32);
-    if (tid < kM) p.eta = ip.eta[(int64_t)blk * kM + tid];
+// buffer resource over `bytes` bytes at `base` (raw, stride 0)
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// per-thread constants of the staging step (its 4 columns and its row)
-struct StageConst {
-    float cs[2], sn[2];     // rotary cos/sin at position `row` for columns c0, c0+1
-    float gam[4], gb[4];    // gamma, gamma*beta for c0, c0+1, c0+32, c0+33
-    float bet[4];
+template <typename Tin>
+struct Raw;
+template <>
+struct Raw<__bf16> {
+    uint2 q, k, v;  // 4 bf16 each
+    float eta;
+    using U = uint2;
+    __device__ static void unpack(uint2 u, float (&x)[4]) {
+        x[0] = __builtin_bit_cast(float, u.x << 16);
+        x[1] = __builtin_bit_cast(float, u.x & 0xffff0000u);
+        x[2] = __builtin_bit_cast(float, u.y << 16);
+        x[3] = __builtin_bit_cast(float, u.y & 0xffff0000u);
+    }
+};
+template <>
+struct Raw<float> {
+    uint4 q, k, v;
+    float eta;
+    using U = uint4;
+    __device__ static void unpack(uint4 u, float (&x)[4]) {
+        x[0] = __builtin_bit_cast(float, u.x);
+        x[1] = __builtin_bit_cast(float, u.y);
+        x[2] = __builtin_bit_cast(float, u.z);
+        x[3] = __builtin_bit_cast(float, u.w);
+    }
 };
 
-template <typename Tin, typename T>
-__device__ __forceinline__ void stage(Stage<T> &S, const Pref<Tin> &p, const StageConst &sc, int rope, int row,
-                                      int c0, int tid) {
-    float q[4], k[4], v[4];
-    Pref<Tin>::unpack(p.q[0], q[0], q[1]);
-    Pref<Tin>::unpack(p.q[1], q[2], q[3]);
-    Pref<Tin>::unpack(p.k[0], k[0], k[1]);
-    Pref<Tin>::unpack(p.k[1], k[2], k[3]);
-    Pref<Tin>::unpack(p.v[0], v[0], v[1]);
-    Pref<Tin>::unpack(p.v[1], v[2], v[3]);
-    if (rope) {
-        // pairs (c, c + 32): first half x*cos - x'*sin, second half x'*cos + x*sin
+// what the LayerNorm phases need of one mini-batch, per lane; the token's
+// learning rate is folded in: u' = eta * gamma * (LN(z) - (v - k)) = eg2 * xhat + cel
+struct RowRegs {
+    float cel[4];   // eta * gamma * (beta - v + k)
+    float eg2[4];   // eta * gamma^2
+    float qres[4];  // q + beta
+};
+
+template <typename Tin, typename Tout, typename T, bool ROPE>
+struct RowWave {
+    const LinearArgs &a;
+    int t, n, rw;  // token row 4rw + g, lane n within the row
+    int N;
+    // per-lane pointers at token row t, column 4n of the first mini-batch of
+    // the call, and elements per mini-batch; the output goes through a
+    // buffer resource (byte offset of the lane, bytes per mini-batch)
+    const Tin *pq, *pk, *pv;
+    const float *pe;
+    int64_t sq, sk, sv;
+    Rsrc ro;
+    uint32_t oo, bo;
+    float gam[4], gam2[4], bet[4], gb[4];
+    float cs[4], sn[4];    // rotary cos and signed sin of columns 4n + e at position t
+
+    __device__ void fetch(Raw<Tin> &r, int blk) const {
+        blk = blk < N ? blk : N - 1;  // past the end: a harmless in-bounds re-read
+        using U = typename Raw<Tin>::U;
+        r.q = *(const U *)(pq + (int64_t)blk * sq);  // blk * s*: wave-uniform
+        r.k = *(const U *)(pk + (int64_t)blk * sk);
+        r.v = *(const U *)(pv + (int64_t)blk * sv);
+        r.eta = pe[(int64_t)blk * kM];
+    }
+
+    // rotary, MFMA row fragments of q and k into LDS, LayerNorm operands into rr
+    __device__ void stage(Stage<T> &S, const Raw<Tin> &r, RowRegs &rr) const {
+        float qv[4], kv[4], vv[4];
+        Raw<Tin>::unpack(r.q, qv);
+        Raw<Tin>::unpack(r.k, kv);
+        Raw<Tin>::unpack(r.v, vv);
+        if constexpr (ROPE) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const float q1 = q[i] * sc.cs[i] - q[i + 2] * sc.sn[i];
-            const float q2 = q[i + 2] * sc.cs[i] + q[i] * sc.sn[i];
-            const float k1 = k[i] * sc.cs[i] - k[i + 2] * sc.sn[i];
-            const float k2 = k[i + 2] * sc.cs[i] + k[i] * sc.sn[i];
-            q[i] = q1;
-            q[i + 2] = q2;
-            k[i] = k1;
-            k[i + 2] = k2;
+            for (int e = 0; e < 4; ++e) {
+                const float qo = row_swap8(qv[e]), ko = row_swap8(kv[e]);
+                qv[e] = qv[e] * cs[e] + qo * sn[e];
+                kv[e] = kv[e] * cs[e] + ko * sn[e];
+            }
+        }
+        Op<T>::put4(&S.qx[t][4 * n], qv[0], qv[1], qv[2], qv[3]);
+        Op<T>::put4(&S.kx[t][4 * n], kv[0], kv[1], kv[2], kv[3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            rr.cel[e] = r.eta * (gam[e] * (kv[e] - vv[e]) + gb[e]);
+            rr.eg2[e] = r.eta * gam2[e];
+            rr.qres[e] = qv[e] + bet[e];
         }
     }
-    Op<T>::put2(&S.qx[row][c0], q[0], q[1]);
-    Op<T>::put2(&S.qx[row][c0 + 32], q[2], q[3]);
-    Op<T>::put2(&S.kx[row][c0], k[0], k[1]);
-    Op<T>::put2(&S.kx[row][c0 + 32], k[2], k[3]);
-    Op<T>::put(&S.kt[c0][row], k[0]);
-    Op<T>::put(&S.kt[c0 + 1][row], k[1]);
-    Op<T>::put(&S.kt[c0 + 32][row], k[2]);
-    Op<T>::put(&S.kt[c0 + 33][row], k[3]);
-    float ce[4], qr[4];
+
+    // LayerNorm backward of Z_nb (row t): ng = -eta * dL/dZ, to the ng tile
+    __device__ void ln_backward(Smem<T> &sm, const RowRegs &rr) const {
+        const f32x4 z = *(const f32x4 *)&sm.zbuf[t][4 * n];
+        const float mu = row_sum16(z[0] + z[1] + z[2] + z[3]) * (1.f / kD);
+        float d[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[e] = z[e] - mu;
+        const float var = row_sum16(d[0] * d[0] + d[1] * d[1] + d[2] * d[2] + d[3] * d[3]) * (1.f / kD);
+        const float rs = __builtin_amdgcn_rsqf(var + a.eps);  // var + eps >= eps > 0
+        float xh[4], u[4], su = 0.f, sux = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            xh[e] = d[e] * rs;
+            u[e] = rr.eg2[e] * xh[e] + rr.cel[e];  // eta * gamma * (LN(z) - (v - k))
+            su += u[e];
+            sux += u[e] * xh[e];
+        }
+        su = row_sum16(su) * (1.f / kD);
+        sux = row_sum16(sux) * (1.f / kD);
+        // ng = -rs * (u - mean(u) - xh * mean(u xh))
+        const float A = -rs;
+        const float C0 = rs * su, C1 = rs * sux;
+        float ng[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ng[e] = u[e] * A + (xh[e] * C1 + C0);
+        Op<T>::put4(&sm.gm[t][4 * n], ng[0], ng[1], ng[2], ng[3]);
+    }
+
+    // LayerNorm forward of Zbar_nb (row t): out = q + LN(Zbar)
+    __device__ void ln_forward(const Smem<T> &sm, const RowRegs &rr, int nb) const {
+        const f32x4 zb = *(const f32x4 *)&sm.zbbuf[nb & 1][t][4 * n];
+        const float mu = row_sum16(zb[0] + zb[1] + zb[2] + zb[3]) * (1.f / kD);
+        float d[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[e] = zb[e] - mu;
+        const float var = row_sum16(d[0] * d[0] + d[1] * d[1] + d[2] * d[2] + d[3] * d[3]) * (1.f / kD);
+        const float rs = __builtin_amdgcn_rsqf(var + a.eps);  // var + eps >= eps > 0
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = d[e] * (rs * gam[e]) + rr.qres[e];
+        const uint32_t so = (uint32_t)nb * bo;
+        if constexpr (std::is_same<Tout, float>::value) {
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{y[0], y[1], y[2], y[3]}), ro, (int)oo,
+                                                   (int)so, 0);
+        } else {
+            typedef __bf16 b4 __attribute__((ext_vector_type(4)));
+            __builtin_amdgcn_raw_buffer_store_b64(
+                __builtin_bit_cast(u32x2, b4{(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]}), ro, (int)oo,
+                (int)so, 0);
+        }
+    }
+};
+
+template <typename Tin, typename Tout, typename T, bool ROPE>
+__device__ void row_main(const LinearArgs &a, Smem<T> &sm, int bi, int hi, int rw, int g, int n) {
+    RowWave<Tin, Tout, T, ROPE> R{a};
+    R.t = 4 * rw + g;
+    R.n = n;
+    R.rw = rw;
+    R.N = a.ntok;
+    const int N = a.ntok;
+    R.pq = (const Tin *)a.q.p + bi * a.q.sB + hi * a.q.sH + (int64_t)(a.t0 + R.t) * a.q.sL + 4 * n;
+    R.pk = (const Tin *)a.k.p + bi * a.k.sB + hi * a.k.sH + (int64_t)(a.t0 + R.t) * a.k.sL + 4 * n;
+    R.pv = (const Tin *)a.v.p + bi * a.v.sB + hi * a.v.sH + (int64_t)(a.t0 + R.t) * a.v.sL + 4 * n;
+    R.pe = a.eta + bi * a.eta_sB + hi * a.eta_sH + a.t0 + R.t;
+    R.sq = kM * a.q.sL;
+    R.sk = kM * a.k.sL;
+    R.sv = kM * a.v.sL;
+    // output rows of this chain from the first token of the call; the host
+    // checks that they span less than 2^31 bytes
+    R.ro = make_rsrc((Tout *)a.out.p + bi * a.out.sB + hi * a.out.sH + (int64_t)a.t0 * a.out.sL, 0x7fffffffu);
+    R.oo = (uint32_t)((R.t * a.out.sL + 4 * n) * (int64_t)sizeof(Tout));
+    R.bo = (uint32_t)(kM * a.out.sL * (int64_t)sizeof(Tout));
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        ce[e] = sc.gam[e] * (k[e] - v[e]) + sc.gb[e];
-        qr[e] = q[e] + sc.bet[e];
+        const int c = 4 * n + e;
+        R.gam[e] = a.ln_w[hi * kD + c];
+        R.bet[e] = a.ln_b[hi * kD + c];
+        R.gam2[e] = R.gam[e] * R.gam[e];
+        R.gb[e] = R.gam[e] * R.bet[e];
+        // whole mini-batches start at multiples of 16: position mod 16 == t
+        const int i = c & 31;
+        const double th = (double)R.t * pow((double)a.rope_base, -2.0 * (double)i / (double)kD);
+        R.cs[e] = (float)cos(th);
+        R.sn[e] = (c < 32 ? -1.f : 1.f) * (float)sin(th);
     }
-    *(float2 *)&S.cel[row][c0] = float2{ce[0], ce[1]};
-    *(float2 *)&S.cel[row][c0 + 32] = float2{ce[2], ce[3]};
-    *(float2 *)&S.qres[row][c0] = float2{qr[0], qr[1]};
-    *(float2 *)&S.qres[row][c0 + 32] = float2{qr[2], qr[3]};
-    if (tid < kM) S.eta[tid] = p.eta;
+
+    Raw<Tin> pf[kRing];  // pf[m % 4]: inputs of mini-batch m, fetched 4 steps ahead
+    RowRegs rr[kRing];   // rr[m % 4]: LayerNorm operands of mini-batch m
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) R.fetch(pf[i], i);
+    R.stage(sm.st[0], pf[0], rr[0]);
+    R.fetch(pf[0], 4);
+    R.stage(sm.st[1], pf[1], rr[1]);
+    R.fetch(pf[1], 5);
+    __syncthreads();  // mini-batches 0, 1 staged
+    R.stage(sm.st[2], pf[2], rr[2]);
+    R.fetch(pf[2], 6);
+    __syncthreads();  // Z_0 written
+    R.ln_backward(sm, rr[0]);
+    __syncthreads();  // ng_0 ready
+
+    // step m (1 <= m < N).  Phase 1 (off the sequential chain, while the
+    // column waves form Z_m): forward LayerNorm of Zbar_m-2, stage m+2, fetch
+    // m+6.  Phase 2: backward LayerNorm of Z_m -> ng_m.
+    // In the loop m = 2 + 4k + i, so every register-set index is static:
+    // slot (m+2) % 4 = (m-2) % 4 = i, slot m % 4 = (2+i) % 4.
+    auto step = [&](int m, auto I) {
+        constexpr int i = decltype(I)::value;
+        R.ln_forward(sm, rr[i], m - 2);
+        // slot i is reused by the staging below: finish reading it first
+        __builtin_amdgcn_sched_barrier(0);
+        R.stage(sm.st[i], pf[i], rr[i]);
+        // consume the register set before refilling it, so the refill lands in
+        // the same registers (no copies that would wait on the new loads)
+        __builtin_amdgcn_sched_barrier(0);
+        R.fetch(pf[i], m + 6);
+        __syncthreads();  // Z_m, Zbar_m-1 written
+        R.ln_backward(sm, rr[(2 + i) % kRing]);
+        __syncthreads();  // ng_m ready
+    };
+    // after the last step, with N = m + r (m = 2 mod 4): Zbar_N-2, Zbar_N-1
+    auto last = [&](auto I) {
+        constexpr int r = decltype(I)::value;
+        R.ln_forward(sm, rr[r % kRing], N - 2);
+        __syncthreads();  // Zbar_N-1 written
+        R.ln_forward(sm, rr[(r + 1) % kRing], N - 1);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    if (N == 1) {
+        __syncthreads();  // Zbar_0 written
+        R.ln_forward(sm, rr[0], 0);
+        return;
+    }
+    // step 1 (nothing to forward yet)
+    R.stage(sm.st[3], pf[3], rr[3]);
+    __builtin_amdgcn_sched_barrier(0);
+    R.fetch(pf[3], 7);
+    __syncthreads();  // Z_1, Zbar_0 written
+    R.ln_backward(sm, rr[1]);
+    __syncthreads();  // ng_1 ready
+    int m = 2;
+    for (; m + 3 < N; m += kRing) {  // branch-free steady state
+        step(m, I0{});
+        step(m + 1, I1{});
+        step(m + 2, I2{});
+        step(m + 3, I3{});
+    }
+    switch (N - m) {  // 0 .. 3 steps left
+    case 0:
+        last(I0{});
+        break;
+    case 1:
+        step(m, I0{});
+        last(I1{});
+        break;
+    case 2:
+        step(m, I0{});
+        step(m + 1, I1{});
+        last(I2{});
+        break;
+    default:
+        step(m, I0{});
+        step(m + 1, I1{});
+        step(m + 2, I2{});
+        last(I3{});
+        break;
+    }
 }
 
 // causal matrix tril(S + 1) from S^T in accumulator layout (lane: query n, keys 4g+j)
@@ -286,255 +503,115 @@ __device__ __forceinline__ f32x4 causal(f32x4 st, int n, int g) {
     return m;
 }
 
-template <typename Tin, typename Tout, typename T>
-__global__ __launch_bounds__(256, 1) void linear_dual_kernel(LinearArgs a) {
+template <typename T>
+__device__ void col_main(const LinearArgs &a, Smem<T> &sm, int ch, int c, int g, int n) {
     using O = Op<T>;
     using F4 = typename O::F4;
     using XF = typename O::XF;
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    Smem<T> &sm = *reinterpret_cast<Smem<T> *>(smem_raw);
+    const int N = a.ntok;
 
-    const int ch = blockIdx.x;
-    const int bi = ch / a.H, hi = ch % a.H;
-    const int tid = threadIdx.x;
-    const int w = tid >> 6, l = tid & 63, g = l >> 4, n = l & 15;
-    const int N = a.ntok;  // whole mini-batches
-
-    // ---- per-thread constants ----
-    const int srow = tid >> 4, c0 = 2 * (tid & 15);
-    StageConst sc;
-    {
-        const int cols[4] = {c0, c0 + 1, c0 + 32, c0 + 33};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            sc.gam[e] = a.ln_w[hi * kD + cols[e]];
-            sc.bet[e] = a.ln_b[hi * kD + cols[e]];
-            sc.gb[e] = sc.gam[e] * sc.bet[e];
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            // blocks are aligned: position mod 16 == row
-            const double th = (double)srow * pow((double)a.rope_base, -2.0 * (double)(c0 + i) / (double)kD);
-            sc.cs[i] = (float)cos(th);
-            sc.sn[i] = (float)sin(th);
-        }
-    }
-    // row-phase constants: row 4w + g, columns 4n .. 4n+3
-    const int rrow = 4 * w + g;
-    float rg[4], rg2[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        rg[e] = a.ln_w[hi * kD + 4 * n + e];
-        rg2[e] = rg[e] * rg[e];
-    }
-
-    InPtr<Tin> ip;
-    ip.q = (const Tin *)a.q.p + bi * a.q.sB + hi * a.q.sH + (int64_t)a.t0 * a.q.sL + c0;
-    ip.k = (const Tin *)a.k.p + bi * a.k.sB + hi * a.k.sH + (int64_t)a.t0 * a.k.sL + c0;
-    ip.v = (const Tin *)a.v.p + bi * a.v.sB + hi * a.v.sH + (int64_t)a.t0 * a.v.sL + c0;
-    ip.eta = a.eta + bi * a.eta_sB + hi * a.eta_sH + a.t0;
-    ip.sq = a.q.sL;
-    ip.sk = a.k.sL;
-    ip.sv = a.v.sL;
-    Tout *op = (Tout *)a.out.p + bi * a.out.sB + hi * a.out.sH + (int64_t)a.t0 * a.out.sL + 4 * n;
-
-    // ---- state: W slab (rows 16r + 4g + j, column 16w + n), bias tile ----
+    // state: W slab (rows 16r + 4g + j, column 16c + n), bias tile
     f32x4 Wt[4], Bt;
     {
         const float *Wc = a.W + (int64_t)ch * kD * kD;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) Wt[r][j] = Wc[(16 * r + 4 * g + j) * kD + 16 * w + n];
-        const float bv = a.b[(int64_t)ch * kD + 16 * w + n];
+            for (int j = 0; j < 4; ++j) Wt[r][j] = Wc[(16 * r + 4 * g + j) * kD + 16 * c + n];
+        const float bv = a.b[(int64_t)ch * kD + 16 * c + n];
         Bt = f32x4{bv, bv, bv, bv};
     }
-    const F4 ones = O::make(1.f, 1.f, 1.f, 1.f);
+    const typename O::Sel sel = O::sel(n, g);
+    const F4 ones = O::make(f32x4{1.f, 1.f, 1.f, 1.f});
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f}, one = {1.f, 1.f, 1.f, 1.f};
 
-    // ---- prologue: mini-batches 0 and 1 staged, 2 .. 2+kAhead-1 in flight ----
-    Pref<Tin> pf[kAhead];
+    f32x4 Y, P;   // Y_m+1 = K_m+1 W_m + b_m ; P_m = Q_m W_m + b_m
+    F4 Mf, Cf;    // tril(Q_m K_m^T + 1), K_m+1 K_m^T + 1 (A fragments)
+    F4 kt[4];     // K_m^T rows 16r .. 16r+15 (A fragments)
+    XF kxn;       // K_m row fragment
+
+    __syncthreads();  // mini-batches 0, 1 staged
     {
-        Pref<Tin> p0, p1;
-        fetch(p0, ip, 0, srow, tid);
-        if (N > 1) fetch(p1, ip, 1, srow, tid);
+        const XF wf = O::cvt_w(Wt);
+        const XF kx0 = O::load_x(&sm.st[0].kx[0][0], n, g);
+        const XF qx0 = O::load_x(&sm.st[0].qx[0][0], n, g);
+        const f32x4 Z0 = O::xx(kx0, wf, Bt);
 #pragma unroll
-        for (int i = 0; i < kAhead; ++i)
-            if (2 + i < N) fetch(pf[(2 + i) % kAhead], ip, 2 + i, srow, tid);
-        stage<Tin, T>(sm.st[0], p0, sc, a.rope, srow, c0, tid);
-        if (N > 1) stage<Tin, T>(sm.st[1], p1, sc, a.rope, srow, c0, tid);
+        for (int j = 0; j < 4; ++j) sm.zbuf[4 * g + j][16 * c + n] = Z0[j];
+        P = O::xx(qx0, wf, Bt);
+        Mf = O::make(causal(O::xx(kx0, qx0, zero), n, g));
+        const XF kx1 = O::load_x(&sm.st[1].kx[0][0], n, g);
+        Y = O::xx(kx1, wf, Bt);
+        Cf = O::make(O::xx(kx0, kx1, one));
+        O::kt_frags(kx0, sel, kt);
+        kxn = kx1;
     }
-    __syncthreads();
+    __syncthreads();  // Z_0 written
+    __syncthreads();  // ng_0 ready
 
-    f32x4 Y, P;  // Y_n+1 = K_n+1 W_n + b_n ; P_n = Q_n W_n + b_n
+    for (int m = 1; m < N; ++m) {
+        // phase 1, the sequential chain: Z_m = Y_m + C_m-1 ng_m-1, and Zbar_m-1
+        const F4 gf = O::load_b(&sm.gm[0][0], 16 * c + n, g);
+        const f32x4 Z = O::mma16(Cf, gf, Y);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sm.zbuf[4 * g + j][16 * c + n] = Z[j];
+        const f32x4 ZB = O::mma16(Mf, gf, P);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sm.zbbuf[(m - 1) & 1][4 * g + j][16 * c + n] = ZB[j];
+        __syncthreads();  // Z_m, Zbar_m-1 written
 
-    // Column phase of mini-batch n: P_n, Y_n+1, and (waves 0/1) the 16x16
-    // matrices of mini-batch n.  Z_0 is written here when n == 0.
-    auto column_products = [&](int nb) {
-        const Stage<T> &S = sm.st[nb % kRing];
-        const typename O::WF wf = O::cvt_w(Wt);
-        const XF qx = O::load_x(&S.qx[0][0], n, g);
-        P = O::xx(qx, wf, Bt);
-        if (nb == 0) {
-            const XF kx = O::load_x(&S.kx[0][0], n, g);
-            const f32x4 Z0 = O::xx(kx, wf, Bt);
+        // phase 2 (row waves run the LayerNorm of Z_m): W_m, b_m, then the
+        // products of mini-batch m with W_m
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sm.zbuf[4 * g + j][16 * w + n] = Z0[j];
-        }
-        if (nb + 1 < N) {
-            const XF kx1 = O::load_x(&sm.st[(nb + 1) % kRing].kx[0][0], n, g);
-            Y = O::xx(kx1, wf, Bt);
-        }
-        if (w == 0) {
-            // S^T[key m][query n'] = k_m . q_n'  ->  lane holds S[n][4g+j]
-            const XF kx = O::load_x(&S.kx[0][0], n, g);
-            const f32x4 st = O::xx(kx, qx, f32x4{0.f, 0.f, 0.f, 0.f});
-            const f32x4 m = causal(st, n, g);
-            sm.mop[l] = O::make(m[0], m[1], m[2], m[3]);
-        } else if (w == 1 && nb + 1 < N) {
-            // C[query i of n+1][key j of n] = k_n+1,i . k_n,j + 1
-            const XF kx = O::load_x(&S.kx[0][0], n, g);
-            const XF kx1 = O::load_x(&sm.st[(nb + 1) % kRing].kx[0][0], n, g);
-            const f32x4 c = O::xx(kx, kx1, f32x4{1.f, 1.f, 1.f, 1.f});
-            sm.cop[l] = O::make(c[0], c[1], c[2], c[3]);
-        }
-    };
-
-    // Row phase, LayerNorm backward of Z_nb: ng = -eta * dL/dZ into gop.
-    auto ln_backward = [&](int nb) {
-        const Stage<T> &S = sm.st[nb % kRing];
-        const f32x4 z = *(const f32x4 *)&sm.zbuf[rrow][4 * n];
-        const f32x4 ce = *(const f32x4 *)&S.cel[rrow][4 * n];
-        const float eta = S.eta[rrow];
-        const float mu = row_sum16(z[0] + z[1] + z[2] + z[3]) * (1.f / kD);
-        f32x4 d;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) d[e] = z[e] - mu;
-        const float var = row_sum16(d[0] * d[0] + d[1] * d[1] + d[2] * d[2] + d[3] * d[3]) * (1.f / kD);
-        const float rs = rsqrtf(var + a.eps);
-        f32x4 xh, u;
-        float su = 0.f, sux = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            xh[e] = d[e] * rs;
-            u[e] = rg2[e] * xh[e] + ce[e];  // gamma * (LN(z) - (v - k))
-            su += u[e];
-            sux += u[e] * xh[e];
-        }
-        su = row_sum16(su) * (1.f / kD);
-        sux = row_sum16(sux) * (1.f / kD);
-        // ng = -eta * rs * (u - mean(u) - xh * mean(u xh))
-        const float A = -eta * rs;
-        const float C0 = -A * su, C1 = -A * sux;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float ng = u[e] * A + (xh[e] * C1 + C0);
-            // token rrow = 4w + g: fragment (column 4n+e, token group w), element g
-            O::put(reinterpret_cast<T *>(&sm.gop[4 * n + e][w]) + g, ng);
-        }
-    };
-
-    // Row phase, LayerNorm forward of Zbar_nb: out = q + LN(Zbar).
-    auto ln_forward = [&](int nb) {
-        const Stage<T> &S = sm.st[nb % kRing];
-        const f32x4 zb = *(const f32x4 *)&sm.zbbuf[rrow][4 * n];
-        const f32x4 qr = *(const f32x4 *)&S.qres[rrow][4 * n];
-        const float mu = row_sum16(zb[0] + zb[1] + zb[2] + zb[3]) * (1.f / kD);
-        f32x4 d;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) d[e] = zb[e] - mu;
-        const float var = row_sum16(d[0] * d[0] + d[1] * d[1] + d[2] * d[2] + d[3] * d[3]) * (1.f / kD);
-        const float rs = rsqrtf(var + a.eps);
-        Tout *o = op + (int64_t)(nb * kM + rrow) * a.out.sL;
-        float y[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = d[e] * (rs * rg[e]) + qr[e];
-        if constexpr (std::is_same<Tout, float>::value) {
-            *(f32x4 *)o = f32x4{y[0], y[1], y[2], y[3]};
-        } else {
-            typedef __bf16 b4 __attribute__((ext_vector_type(4)));
-            *(b4 *)o = b4{(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
-        }
-    };
-
-    // Column phase 1 of mini-batch nb (nb >= 1): consume ng_nb-1.
-    auto apply_step = [&](int nb, bool last) {
-        const Stage<T> &Sp = sm.st[(nb - 1) % kRing];
-        const F4 gf = sm.gop[16 * w + n][g];
-        if (!last) {
-            const f32x4 Z = O::mma16(sm.cop[l], gf, Y);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sm.zbuf[4 * g + j][16 * w + n] = Z[j];
-        }
-        const f32x4 ZB = O::mma16(sm.mop[l], gf, P);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sm.zbbuf[4 * g + j][16 * w + n] = ZB[j];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const F4 kt = *(const F4 *)&Sp.kt[16 * r + n][4 * g];
-            Wt[r] = O::mma16(kt, gf, Wt[r]);
-        }
+        for (int r = 0; r < 4; ++r) Wt[r] = O::mma16(kt[r], gf, Wt[r]);
         Bt = O::mma16(ones, gf, Bt);
-    };
-
-    auto stage_ahead = [&](int nb, Pref<Tin> &pr) {
-        // stage mini-batch nb + 2 from registers, fetch nb + 2 + kAhead
-        if (nb + 2 < N) {
-            stage<Tin, T>(sm.st[(nb + 2) % kRing], pr, sc, a.rope, srow, c0, tid);
-            if (nb + 2 + kAhead < N) fetch(pr, ip, nb + 2 + kAhead, srow, tid);
-        }
-    };
-
-    // ---- mini-batch 0: Z_0 directly, then its LayerNorm backward ----
-    column_products(0);
-    __syncthreads();
-    ln_backward(0);
-    stage_ahead(0, pf[2 % kAhead]);
-    __syncthreads();
-
-    // ---- steady state ----
-    auto iteration = [&](int nb, Pref<Tin> &pr) {
-        apply_step(nb, false);  // Z_nb, Zbar_nb-1, W_nb, b_nb
-        __syncthreads();
-        column_products(nb);    // P_nb, Y_nb+1, M_nb, C_nb
-        ln_backward(nb);        // ng_nb
-        ln_forward(nb - 1);     // out_nb-1
-        stage_ahead(nb, pr);
-        __syncthreads();
-    };
-    // register set of mini-batch m is pf[m % kAhead]; nb = 1 + kAhead*i here
-    static_assert(kAhead == 3, "the unrolled loop below names the register sets");
-    int nb = 1;
-    for (; nb + kAhead <= N; nb += kAhead) {
-        iteration(nb, pf[0]);
-        iteration(nb + 1, pf[1]);
-        iteration(nb + 2, pf[2]);
+        const XF wf = O::cvt_w(Wt);
+        const XF qx = O::load_x(&sm.st[m % kRing].qx[0][0], n, g);
+        const XF kx1 = O::load_x(&sm.st[(m + 1) % kRing].kx[0][0], n, g);  // stale past the end: unused
+        P = O::xx(qx, wf, Bt);
+        Y = O::xx(kx1, wf, Bt);
+        Mf = O::make(causal(O::xx(kxn, qx, zero), n, g));
+        Cf = O::make(O::xx(kxn, kx1, one));
+        O::kt_frags(kxn, sel, kt);
+        kxn = kx1;
+        __syncthreads();  // ng_m ready
     }
-    // fewer than kAhead mini-batches left: nb >= N - 2, nothing left to stage
-    for (; nb < N; ++nb) {
-        apply_step(nb, false);
-        __syncthreads();
-        column_products(nb);
-        ln_backward(nb);
-        ln_forward(nb - 1);
-        __syncthreads();
+    {
+        const F4 gf = O::load_b(&sm.gm[0][0], 16 * c + n, g);
+        const f32x4 ZB = O::mma16(Mf, gf, P);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sm.zbbuf[(N - 1) & 1][4 * g + j][16 * c + n] = ZB[j];
+        __syncthreads();  // Zbar_N-1 written
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Wt[r] = O::mma16(kt[r], gf, Wt[r]);
+        Bt = O::mma16(ones, gf, Bt);
     }
-
-    // ---- epilogue: Zbar of the last mini-batch, final step ----
-    apply_step(N, true);
-    __syncthreads();
-    ln_forward(N - 1);
 
     float *Wo = a.W + (int64_t)ch * kD * kD;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) Wo[(16 * r + 4 * g + j) * kD + 16 * w + n] = Wt[r][j];
-    if (g == 0) a.b[(int64_t)ch * kD + 16 * w + n] = Bt[0];
+        for (int j = 0; j < 4; ++j) Wo[(16 * r + 4 * g + j) * kD + 16 * c + n] = Wt[r][j];
+    if (g == 0) a.b[(int64_t)ch * kD + 16 * c + n] = Bt[0];
 }
 
-template <typename Tin, typename Tout, typename T>
+template <typename Tin, typename Tout, typename T, bool ROPE>
+__global__ __launch_bounds__(512, 1) void linear_dual_kernel(LinearArgs a) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    Smem<T> &sm = *reinterpret_cast<Smem<T> *>(smem_raw);
+    const int ch = blockIdx.x;
+    const int bi = ch / a.H, hi = ch % a.H;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, n = l & 15;
+    // both roles pass the same sequence of 2N + 2 barriers
+    if (w < 4)
+        col_main<T>(a, sm, ch, w, g, n);
+    else
+        row_main<Tin, Tout, T, ROPE>(a, sm, bi, hi, w - 4, g, n);
+}
+
+template <typename Tin, typename Tout, typename T, bool ROPE>
 hipError_t launch_typed(const LinearArgs &a, hipStream_t s) {
-    const void *fn = (const void *)&linear_dual_kernel<Tin, Tout, T>;
+    const void *fn = (const void *)&linear_dual_kernel<Tin, Tout, T, ROPE>;
     const size_t lds = sizeof(Smem<T>);
     static bool configured = false;  // per instantiation
     if (!configured) {
@@ -542,17 +619,22 @@ hipError_t launch_typed(const LinearArgs &a, hipStream_t s) {
         if (e != hipSuccess) return e;
         configured = true;
     }
-    hipLaunchKernelGGL((linear_dual_kernel<Tin, Tout, T>), dim3(a.B * a.H), dim3(256), lds, s, a);
+    hipLaunchKernelGGL((linear_dual_kernel<Tin, Tout, T, ROPE>), dim3(a.B * a.H), dim3(512), lds, s, a);
     return hipGetLastError();
+}
+
+template <typename Tin, typename Tout, typename T>
+hipError_t launch_rope(const LinearArgs &a, hipStream_t s) {
+    return a.rope ? launch_typed<Tin, Tout, T, true>(a, s) : launch_typed<Tin, Tout, T, false>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_linear_dual(const LinearArgs &a, int in_bf16, int out_bf16, hipStream_t s) {
-    if (in_bf16 && out_bf16) return launch_typed<__bf16, __bf16, _Float16>(a, s);
-    if (in_bf16) return launch_typed<__bf16, float, _Float16>(a, s);
-    if (out_bf16) return launch_typed<float, __bf16, float>(a, s);
-    return launch_typed<float, float, float>(a, s);
+    if (in_bf16 && out_bf16) return launch_rope<__bf16, __bf16, _Float16>(a, s);
+    if (in_bf16) return launch_rope<__bf16, float, _Float16>(a, s);
+    if (out_bf16) return launch_rope<float, __bf16, float>(a, s);
+    return launch_rope<float, float, float>(a, s);
 }
 
 }  // namespace ttt

@@ -214,7 +214,18 @@ ttt_status linear_call(Mode mode, const ttt_linear_cfg *cfg, int32_t L, const Ac
         a.ntok = body;
         a.t0 = head;
         a.pos0 = st->offset + head;
-        if ((e = launch_linear_dual(a, in_bf16, out_bf16, hs)) != hipSuccess) return hip_fail(e, "dual kernel");
+        // the dual kernel addresses each chain's rows with 32-bit byte offsets
+        const int64_t rows = (int64_t)body * K;
+        const size_t ei = dtype_size(cfg->in_dtype), eo = dtype_size(cfg->out_dtype);
+        const int64_t span = std::max({(rows - 1) * x.XQ.sL * (int64_t)ei, (rows - 1) * x.XK.sL * (int64_t)ei,
+                                       (rows - 1) * x.XV.sL * (int64_t)ei, (rows - 1) * x.out.sL * (int64_t)eo}) +
+                             (int64_t)cfg->D * 4;
+        if (span < (int64_t)INT32_MAX) {
+            if ((e = launch_linear_dual(a, in_bf16, out_bf16, hs)) != hipSuccess) return hip_fail(e, "dual kernel");
+        } else {
+            a.ntok = body * K;  // token by token: same result, no 32-bit offsets
+            if ((e = launch_linear_token(a, in_bf16, out_bf16, hs)) != hipSuccess) return hip_fail(e, "token kernel");
+        }
     }
     if (tail > 0) {
         a.ntok = tail;

@@ -1,0 +1,490 @@
+// mlp_dual.hip -- TTT-MLP over mini-batches of 16 tokens in the dual form.
+//
+// The hidden state is a two-layer MLP f(x) = GELU(x W1 + b1) W2 + b2
+// (D = 64 -> F = 256 -> D), the TTT-Linear step applied to each layer
+// ("代码连连看——TTT": TTT-MLP is TTT-Linear stacked twice; README: the hidden
+// state of TTT-MLP is a two-layer MLP).  Per mini-batch (K rows X = k, Q, V):
+//   Z1 = X W1 + b1, X2 = GELU(Z1), Z2 = X2 W2 + b2
+//   ng2 = -eta * d/dZ2 of 1/2 ||LN(Z2) - (V - X)||^2
+//   ng1 = (ng2 W2^T) o GELU'(Z1)
+//   Zb1 = Q W1 + b1 + tril(Q X^T + 1) ng1,  Xb2 = GELU(Zb1)
+//   Zb2 = Xb2 W2 + b2 + tril(Xb2 X2^T + 1) ng2,  out = Q + LN(Zb2)
+//   W1 += X^T ng1, b1 += 1^T ng1, W2 += X2^T ng2, b2 += 1^T ng2
+// A trailing partial mini-batch (r < 16 tokens) runs with eta = 0 on the
+// missing rows; its step is not applied: the accumulated gradients go to
+// the *_grad state instead (an open mini-batch).
+//
+// Design (gfx950, one workgroup of 8 waves per (batch, head)):
+//  * wave w owns hidden units f in [32w, 32w+32): its 64x32 slab of W1 and
+//    its 32x64 slab of W2, as fp32 MFMA accumulator tiles for the whole
+//    chain; the backward product ng2 W2^T contracts over the other index of
+//    W2, so each mini-batch also leaves an fp16 row copy of W2 in LDS;
+//  * Z1, Zb1, ng1, X2 stay in registers in accumulator layout, which is also
+//    the operand layout of the M1 ng1 correction and of the three state
+//    updates; X2, Xb2 and ng2 go through LDS where a row layout is needed;
+//  * Z2 and Zb2 are sums over the 8 hidden slices: partial tiles in LDS,
+//    summed by the LayerNorm waves 0..3 (16 lanes per token row, DPP sums);
+//  * operands are fp16 (bf16 inputs), accumulation fp32; GELU is exact (erf).
+#include <type_traits>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace ttt {
+namespace {
+
+constexpr int kM = 16;
+constexpr int kF = 256;
+constexpr int XP = 72;    // f16 row pitch of the 16x64 tiles
+constexpr int HP = 264;   // f16 row pitch of the 16x256 tiles
+constexpr int NP = 68;    // f16 row pitch of the ng2 tile
+constexpr int FP = 68;    // fp32 row pitch of the partial sums
+constexpr int kParts = 9; // 8 hidden slices + the causal term of Zb2
+
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+
+struct Smem {
+    _Float16 xs[2][kM][XP];   // K rows (rotated), double-buffered by mini-batch
+    _Float16 qs[2][kM][XP];   // Q rows (rotated)
+    _Float16 x2[kM][HP];      // X2 = GELU(Z1), [token][hidden]
+    _Float16 xb2[kM][HP];     // Xb2 = GELU(Zb1)
+    _Float16 ng2[kM][NP];     // ng2, [token][d]
+    _Float16 w2h[kF][XP];     // W2 at the start of the mini-batch, [hidden][d]
+    float part[kParts][kM][FP];  // partial sums of Z2 / Zb2, [slice][token][d]
+    float b2[kD];             // b2 at the start of the current mini-batch
+    float b2n[kD];            // b2 after its step
+    float gam[kD], gam2[kD], bet[kD], gb[kD];  // per-column LayerNorm constants
+    float cs[kM][kD], sn[kM][kD];            // rotary cos / signed sin at position t, column c
+};
+
+__device__ __forceinline__ f32x4 mfma32(h8 a, h8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(h4 a, h4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ h4 to_h4(f32x4 x) {
+    return h4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+}
+// two accumulator tiles (rows 4g+j and 16+4g+j) as a 16x16x32 B operand whose
+// k slot 8g+i carries row 4g+i (i < 4) or 16+4g+i-4 (i >= 4)
+__device__ __forceinline__ h8 pair_b(f32x4 lo, f32x4 hi) {
+    return h8{(_Float16)lo[0], (_Float16)lo[1], (_Float16)lo[2], (_Float16)lo[3],
+              (_Float16)hi[0], (_Float16)hi[1], (_Float16)hi[2], (_Float16)hi[3]};
+}
+// row n of a row-major f16 tile, columns c0 + {4g..4g+3, 16+4g..16+4g+3}
+// (the same k permutation)
+__device__ __forceinline__ h8 row_perm(const _Float16 *X, int pitch, int n, int g, int c0) {
+    const h4 a = *(const h4 *)(X + n * pitch + c0 + 4 * g);
+    const h4 b = *(const h4 *)(X + n * pitch + c0 + 16 + 4 * g);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// column c of a row-major f16 tile, tokens 4g..4g+3 (a k = 16 operand)
+__device__ __forceinline__ h4 col4(const _Float16 *X, int pitch, int c, int g) {
+    return h4{X[(4 * g) * pitch + c], X[(4 * g + 1) * pitch + c], X[(4 * g + 2) * pitch + c],
+              X[(4 * g + 3) * pitch + c]};
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);
+    x += dpp<0x140>(x);
+    return x;
+}
+
+// exact GELU and its derivative
+__device__ __forceinline__ float gelu(float x) { return 0.5f * x * (1.f + erff(x * 0.70710678118654752f)); }
+__device__ __forceinline__ float gelu_grad(float x) {
+    return 0.5f * (1.f + erff(x * 0.70710678118654752f)) + x * 0.39894228040143268f * expf(-0.5f * x * x);
+}
+
+template <typename Tin, typename Tout, bool ROPE>
+__global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
+    const int ch = blockIdx.x;
+    const int bi = ch / a.H, hi = ch % a.H;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, n = l & 15;
+    const int NB = a.nblk;  // mini-batches; the last has a.tail tokens if a.tail > 0
+    const bool lnw = w < 4; // LayerNorm / staging wave: token row 4w+g, columns 4n..4n+3
+    const int t = 4 * w + g;
+
+    // ---- state of hidden slice f in [32w, 32w+32) ----
+    const int64_t cD = (int64_t)ch * kD;
+    const float *W1g = a.W1 + cD * kF, *W2g = a.W2 + cD * kF;
+    f32x4 W1s[2][4], W2s[2][4], b1t[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int f0 = 32 * w + 16 * s;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                W1s[s][r][j] = W1g[(16 * r + 4 * g + j) * kF + f0 + n];   // W1[d][f]
+                W2s[s][r][j] = W2g[(f0 + 4 * g + j) * kD + 16 * r + n];   // W2[f][d]
+            }
+        const float bv = a.b1[(int64_t)ch * kF + f0 + n];
+        b1t[s] = f32x4{bv, bv, bv, bv};
+    }
+    if (threadIdx.x < kD) sm.b2[threadIdx.x] = a.b2[cD + threadIdx.x];
+
+    // ---- per-column constants (LayerNorm, rotary at position t = row) ----
+    for (int i = threadIdx.x; i < kD; i += 512) {
+        const float gv = a.ln_w[hi * kD + i], bv = a.ln_b[hi * kD + i];
+        sm.gam[i] = gv;
+        sm.gam2[i] = gv * gv;
+        sm.bet[i] = bv;
+        sm.gb[i] = gv * bv;
+    }
+    for (int i = threadIdx.x; i < kM * kD; i += 512) {
+        const int r = i / kD, c = i % kD;
+        const double th = (double)r * pow((double)a.rope_base, -2.0 * (double)(c & 31) / (double)kD);
+        sm.cs[r][c] = (float)cos(th);
+        sm.sn[r][c] = (c < 32 ? -1.f : 1.f) * (float)sin(th);
+    }
+    const Tin *pq = (const Tin *)a.q.p + bi * a.q.sB + hi * a.q.sH + (int64_t)(a.t0 + t) * a.q.sL + 4 * n;
+    const Tin *pk = (const Tin *)a.k.p + bi * a.k.sB + hi * a.k.sH + (int64_t)(a.t0 + t) * a.k.sL + 4 * n;
+    const Tin *pv = (const Tin *)a.v.p + bi * a.v.sB + hi * a.v.sH + (int64_t)(a.t0 + t) * a.v.sL + 4 * n;
+    const float *pe = a.eta + bi * a.eta_sB + hi * a.eta_sH + a.t0 + t;
+    Tout *po = (Tout *)a.out.p + bi * a.out.sB + hi * a.out.sH + (int64_t)(a.t0 + t) * a.out.sL + 4 * n;
+
+    // inputs of one mini-batch for this lane (raw), and the LayerNorm operands
+    using Raw = typename std::conditional<std::is_same<Tin, __bf16>::value, uint2, uint4>::type;
+    struct In {
+        Raw q, k, v;
+        float eta;
+    };
+    auto fetch = [&](In &x, int nb) {
+        // rows past the last token (partial last mini-batch) read nothing and
+        // get eta = 0, so they contribute no gradient
+        const bool valid = !(nb == NB - 1 && a.tail > 0 && t >= a.tail);
+        const int64_t tk = (int64_t)nb * kM;
+        x.q = Raw{};
+        x.k = Raw{};
+        x.v = Raw{};
+        x.eta = 0.f;
+        if (valid) {
+            x.q = *(const Raw *)(pq + tk * a.q.sL);
+            x.k = *(const Raw *)(pk + tk * a.k.sL);
+            x.v = *(const Raw *)(pv + tk * a.v.sL);
+            x.eta = pe[tk];
+        }
+    };
+    auto unpack = [](const Raw &u, float (&x)[4]) {
+        if constexpr (std::is_same<Tin, __bf16>::value) {
+            x[0] = __builtin_bit_cast(float, u.x << 16);
+            x[1] = __builtin_bit_cast(float, u.x & 0xffff0000u);
+            x[2] = __builtin_bit_cast(float, u.y << 16);
+            x[3] = __builtin_bit_cast(float, u.y & 0xffff0000u);
+        } else {
+            x[0] = __builtin_bit_cast(float, u.x);
+            x[1] = __builtin_bit_cast(float, u.y);
+            x[2] = __builtin_bit_cast(float, u.z);
+            x[3] = __builtin_bit_cast(float, u.w);
+        }
+    };
+    float cel[4], eg2[4], qres[4];
+    auto stage = [&](const In &x, int buf) {
+        float q[4], k[4], v[4];
+        unpack(x.q, q);
+        unpack(x.k, k);
+        unpack(x.v, v);
+        if constexpr (ROPE) {
+            const f32x4 c4 = *(const f32x4 *)&sm.cs[t][4 * n], s4 = *(const f32x4 *)&sm.sn[t][4 * n];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float qo = dpp<0x128>(q[e]), ko = dpp<0x128>(k[e]);
+                q[e] = q[e] * c4[e] + qo * s4[e];
+                k[e] = k[e] * c4[e] + ko * s4[e];
+            }
+        }
+        *(h4 *)&sm.qs[buf][t][4 * n] = h4{(_Float16)q[0], (_Float16)q[1], (_Float16)q[2], (_Float16)q[3]};
+        *(h4 *)&sm.xs[buf][t][4 * n] = h4{(_Float16)k[0], (_Float16)k[1], (_Float16)k[2], (_Float16)k[3]};
+        const f32x4 gm = *(const f32x4 *)&sm.gam[4 * n], g2 = *(const f32x4 *)&sm.gam2[4 * n];
+        const f32x4 bt = *(const f32x4 *)&sm.bet[4 * n], gbv = *(const f32x4 *)&sm.gb[4 * n];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            cel[e] = x.eta * (gm[e] * (k[e] - v[e]) + gbv[e]);
+            eg2[e] = x.eta * g2[e];
+            qres[e] = q[e] + bt[e];
+        }
+    };
+
+    In pre;
+    if (lnw) fetch(pre, 0);
+    __syncthreads();  // constants in LDS
+    if (lnw) {
+        stage(pre, 0);
+        if (NB > 1) fetch(pre, 1);
+    }
+    // selection patterns for K^T fragments (see the TTT-Linear kernel)
+    h8 sel[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            sel[h][i] = (i / 4 == h && 4 * g + (i & 3) == n) ? (_Float16)1.f : (_Float16)0.f;
+    const h4 ones = h4{(_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f};
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    __syncthreads();
+
+    // operands of the last step, kept for an open last mini-batch
+    h4 kt[4], n1k[2], x2h[2], G2[4];
+    for (int nb = 0; nb < NB; ++nb) {
+        const int buf = nb & 1;
+        const bool open = (nb == NB - 1) && a.tail > 0;  // partial last mini-batch: keep W, emit grads
+
+        // ---- P0: Z1, P1 = Q W1 + b1, GELU, M1, K^T fragments ----
+        const h8 xp0 = row_perm(&sm.xs[buf][0][0], XP, n, g, 0), xp1 = row_perm(&sm.xs[buf][0][0], XP, n, g, 32);
+        const h8 qp0 = row_perm(&sm.qs[buf][0][0], XP, n, g, 0), qp1 = row_perm(&sm.qs[buf][0][0], XP, n, g, 32);
+        f32x4 X2[2], D1[2], P1[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const h8 wb0 = pair_b(W1s[s][0], W1s[s][1]), wb1 = pair_b(W1s[s][2], W1s[s][3]);
+            const f32x4 z1 = mfma32(xp1, wb1, mfma32(xp0, wb0, b1t[s]));
+            P1[s] = mfma32(qp1, wb1, mfma32(qp0, wb0, b1t[s]));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                X2[s][j] = gelu(z1[j]);
+                D1[s][j] = gelu_grad(z1[j]);
+                sm.x2[4 * g + j][32 * w + 16 * s + n] = (_Float16)X2[s][j];
+            }
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sm.w2h[32 * w + 16 * s2 + 4 * g + j][16 * r + n] = (_Float16)W2s[s2][r][j];
+        h4 M1;
+        {
+            const f32x4 st = mfma32(xp1, qp1, mfma32(xp0, qp0, zero));  // lane: S[query n][key 4g+j]
+            f32x4 m;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) m[j] = (4 * g + j <= n) ? st[j] + 1.f : 0.f;
+            M1 = to_h4(m);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) kt[r] = to_h4(mfma32(r < 2 ? xp0 : xp1, sel[r & 1], zero));
+        if (nb > 0 && threadIdx.x < kD) sm.b2[threadIdx.x] = sm.b2n[threadIdx.x];  // previous step
+        __syncthreads();  // B1: X2 in LDS, b2 current
+
+        // ---- P1: partial Z2 over this hidden slice ----
+        const h8 x2p = row_perm(&sm.x2[0][0], HP, n, g, 32 * w);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const f32x4 z2 = mfma32(x2p, pair_b(W2s[0][r], W2s[1][r]), zero);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sm.part[w][4 * g + j][16 * r + n] = z2[j];
+        }
+        __syncthreads();  // B2
+
+        // ---- P2: Z2 = sum of slices + b2; LayerNorm backward -> ng2 ----
+        if (lnw) {
+            f32x4 z = *(const f32x4 *)&sm.b2[4 * n];
+#pragma unroll
+            for (int p = 0; p < 8; ++p) z += *(const f32x4 *)&sm.part[p][t][4 * n];
+            const float mu = row_sum16(z[0] + z[1] + z[2] + z[3]) * (1.f / kD);
+            float d[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d[e] = z[e] - mu;
+            const float var = row_sum16(d[0] * d[0] + d[1] * d[1] + d[2] * d[2] + d[3] * d[3]) * (1.f / kD);
+            const float rs = __builtin_amdgcn_rsqf(var + a.eps);
+            float xh[4], u[4], su = 0.f, sux = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                xh[e] = d[e] * rs;
+                u[e] = eg2[e] * xh[e] + cel[e];
+                su += u[e];
+                sux += u[e] * xh[e];
+            }
+            su = row_sum16(su) * (1.f / kD);
+            sux = row_sum16(sux) * (1.f / kD);
+            float ng[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ng[e] = -rs * (u[e] - su - xh[e] * sux);
+            *(h4 *)&sm.ng2[t][4 * n] = h4{(_Float16)ng[0], (_Float16)ng[1], (_Float16)ng[2], (_Float16)ng[3]};
+        }
+        __syncthreads();  // B3: ng2 in LDS
+
+        // ---- P3: ng1, Zb1, Xb2; step of W1, b1, b2 ----
+        const h8 gp0 = row_perm(&sm.ng2[0][0], NP, n, g, 0), gp1 = row_perm(&sm.ng2[0][0], NP, n, g, 32);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) G2[r] = col4(&sm.ng2[0][0], NP, 16 * r + n, g);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            // ng1 = (ng2 W2^T) o GELU'(Z1): A = ng2 rows, B = rows f of W2 (k = d)
+            const int f = 32 * w + 16 * s + n;
+            const f32x4 g1 =
+                mfma32(gp1, row_perm(&sm.w2h[0][0], XP, f, g, 32), mfma32(gp0, row_perm(&sm.w2h[0][0], XP, f, g, 0), zero));
+            f32x4 ng1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ng1[j] = g1[j] * D1[s][j];
+            const h4 n1 = to_h4(ng1);
+            const f32x4 zb1 = mfma16(M1, n1, P1[s]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sm.xb2[4 * g + j][32 * w + 16 * s + n] = (_Float16)gelu(zb1[j]);
+            x2h[s] = to_h4(X2[s]);
+            n1k[s] = n1;
+            if (!open) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) W1s[s][r] = mfma16(kt[r], n1, W1s[s][r]);  // W1 += X^T ng1
+                b1t[s] = mfma16(ones, n1, b1t[s]);
+            }
+        }
+        if (w == 0) {
+            // b2 after the step: b2 + column sums of ng2
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float bv = sm.b2[16 * r + n];
+                const f32x4 bn = mfma16(ones, G2[r], f32x4{bv, bv, bv, bv});
+                if (g == 0) sm.b2n[16 * r + n] = bn[0];
+            }
+        }
+        __syncthreads();  // B4: Xb2 in LDS
+
+        // ---- P4: partial Zb2 over this hidden slice; the causal term ----
+        {
+            const h8 xb2p = row_perm(&sm.xb2[0][0], HP, n, g, 32 * w);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const f32x4 z = mfma32(xb2p, pair_b(W2s[0][r], W2s[1][r]), zero);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sm.part[w][4 * g + j][16 * r + n] = z[j];
+            }
+        }
+        // step of W2 (W2 += X2^T ng2), after its last use at the block start
+        if (!open) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) W2s[s][r] = mfma16(x2h[s], G2[r], W2s[s][r]);
+        }
+        if (w == 4) {
+            // M2 = tril(Xb2 X2^T + 1) over all 256 hidden units, then M2 ng2
+            f32x4 st = zero;
+#pragma unroll
+            for (int c = 0; c < kF; c += 32)
+                st = mfma32(row_perm(&sm.x2[0][0], HP, n, g, c), row_perm(&sm.xb2[0][0], HP, n, g, c), st);
+            f32x4 m;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) m[j] = (4 * g + j <= n) ? st[j] + 1.f : 0.f;
+            const h4 M2 = to_h4(m);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const f32x4 z = mfma16(M2, G2[r], zero);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sm.part[8][4 * g + j][16 * r + n] = z[j];
+            }
+        }
+        __syncthreads();  // B5
+
+        // ---- P5: Zb2, out = q + LN(Zb2); stage the next mini-batch ----
+        if (lnw) {
+            f32x4 z = *(const f32x4 *)&sm.b2[4 * n];
+#pragma unroll
+            for (int p = 0; p < kParts; ++p) z += *(const f32x4 *)&sm.part[p][t][4 * n];
+            const float mu = row_sum16(z[0] + z[1] + z[2] + z[3]) * (1.f / kD);
+            float d[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d[e] = z[e] - mu;
+            const float var = row_sum16(d[0] * d[0] + d[1] * d[1] + d[2] * d[2] + d[3] * d[3]) * (1.f / kD);
+            const float rs = __builtin_amdgcn_rsqf(var + a.eps);
+            const f32x4 gm = *(const f32x4 *)&sm.gam[4 * n];
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = d[e] * (rs * gm[e]) + qres[e];
+            const bool valid = !(open && t >= a.tail);
+            if (valid) {
+                Tout *o = po + (int64_t)nb * kM * a.out.sL;
+                if constexpr (std::is_same<Tout, float>::value) {
+                    *(float4 *)o = float4{y[0], y[1], y[2], y[3]};
+                } else {
+                    typedef __bf16 b4 __attribute__((ext_vector_type(4)));
+                    *(b4 *)o = b4{(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
+                }
+            }
+            if (nb + 1 < NB) {
+                stage(pre, buf ^ 1);
+                if (nb + 2 < NB) fetch(pre, nb + 2);
+            }
+        }
+        __syncthreads();  // next mini-batch staged; part, x2, xb2, ng2 free
+    }
+
+    // ---- final state (an open last mini-batch left W, b at its start) ----
+    const bool open_end = a.tail > 0;
+    if (open_end) {
+        // the pages' accumulated gradients of the open mini-batch: -step
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int f0 = 32 * w + 16 * s;
+            float *g1p = a.W1g + cD * kF + (4 * g) * kF + f0 + n;
+            float *g2p = a.W2g + cD * kF + (f0 + 4 * g) * kD + n;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const f32x4 d1 = mfma16(kt[r], n1k[s], zero), d2 = mfma16(x2h[s], G2[r], zero);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    g1p[(16 * r + j) * kF] = -d1[j];
+                    g2p[j * kD + 16 * r] = -d2[j];
+                }
+            }
+            const f32x4 db = mfma16(ones, n1k[s], zero);
+            if (g == 0) a.b1g[(int64_t)ch * kF + f0 + n] = -db[0];
+        }
+    }
+    if (threadIdx.x < kD) {
+        const int d = threadIdx.x;
+        // closed: b2 after the last step; open: b2 at the open block's start
+        a.b2[cD + d] = open_end ? sm.b2[d] : sm.b2n[d];
+        if (open_end) a.b2g[cD + d] = -(sm.b2n[d] - sm.b2[d]);
+    }
+    float *W1o = a.W1 + cD * kF, *W2o = a.W2 + cD * kF;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int f0 = 32 * w + 16 * s;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                W1o[(16 * r + 4 * g + j) * kF + f0 + n] = W1s[s][r][j];
+                W2o[(f0 + 4 * g + j) * kD + 16 * r + n] = W2s[s][r][j];
+            }
+        if (g == 0) a.b1[(int64_t)ch * kF + f0 + n] = b1t[s][0];
+    }
+}
+
+template <typename Tin, typename Tout, bool ROPE>
+hipError_t launch_typed(const MlpArgs &a, hipStream_t s) {
+    const void *fn = (const void *)&mlp_dual_kernel<Tin, Tout, ROPE>;
+    static bool configured = false;
+    if (!configured) {
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Smem));
+        if (e != hipSuccess) return e;
+        configured = true;
+    }
+    hipLaunchKernelGGL((mlp_dual_kernel<Tin, Tout, ROPE>), dim3(a.B * a.H), dim3(512), sizeof(Smem), s, a);
+    return hipGetLastError();
+}
+
+template <typename Tin, typename Tout>
+hipError_t launch_rope(const MlpArgs &a, hipStream_t s) {
+    return a.rope ? launch_typed<Tin, Tout, true>(a, s) : launch_typed<Tin, Tout, false>(a, s);
+}
+
+}  // namespace
+
+// bf16 inputs only (the fp16 operand rounding is sized for them)
+hipError_t launch_mlp_dual(const MlpArgs &a, int in_bf16, int out_bf16, hipStream_t s) {
+    if (!in_bf16) return hipErrorInvalidValue;
+    return out_bf16 ? launch_rope<__bf16, __bf16>(a, s) : launch_rope<__bf16, float>(a, s);
+}
+
+}  // namespace ttt

@@ -151,6 +151,38 @@ ttt_status check_linear_state(const ttt_linear_cfg *cfg, const ttt_linear_state 
     return TTT_OK;
 }
 
+ttt_status check_mlp_cfg(const ttt_mlp_cfg *cfg) {
+    if (!cfg) return fail(TTT_ERR_NULL, "cfg is NULL");
+    ttt_status s;
+    if ((s = check_common(cfg->B, cfg->H, cfg->D, cfg->K, cfg->in_dtype, cfg->out_dtype, cfg->ln_eps,
+                          cfg->rope_base, cfg->rope)))
+        return s;
+    if (cfg->F != 256) return fail(TTT_ERR_SHAPE, "MLP hidden width F=%d unsupported (must be 256)", cfg->F);
+    if (cfg->K != 16) return fail(TTT_ERR_SHAPE, "TTT-MLP needs mini_batch_size 16 (K=%d)", cfg->K);
+    if (cfg->in_dtype != TTT_BF16)
+        return fail(TTT_ERR_UNSUPPORTED, "TTT-MLP takes bf16 inputs (its products run on fp16 operands)");
+    return TTT_OK;
+}
+
+ttt_status check_mlp_state(const ttt_mlp_cfg *cfg, const ttt_mlp_state *st, std::vector<Range> &ranges,
+                           bool check_offset) {
+    if (!st) return fail(TTT_ERR_NULL, "state is NULL");
+    float *const p[8] = {st->W1, st->b1, st->W2, st->b2, st->W1_grad, st->b1_grad, st->W2_grad, st->b2_grad};
+    for (float *q : p) {
+        if (!q) return fail(TTT_ERR_NULL, "state buffer is NULL");
+        if (!aligned16(q)) return fail(TTT_ERR_ALIGN, "state buffers must be 16-byte aligned");
+    }
+    if (check_offset && st->offset < 0) return fail(TTT_ERR_STATE, "state offset %lld < 0", (long long)st->offset);
+    const int64_t n = (int64_t)cfg->B * cfg->H, D = cfg->D, F = cfg->F;
+    const int64_t sz[8] = {D * F, F, F * D, D, D * F, F, F * D, D};
+    ranges.clear();
+    for (int i = 0; i < 8; ++i) ranges.push_back(flat_range(p[i], n * sz[i], 4));
+    for (size_t i = 0; i < ranges.size(); ++i)
+        for (size_t j = i + 1; j < ranges.size(); ++j)
+            if (overlap(ranges[i], ranges[j])) return fail(TTT_ERR_ALIAS, "state buffers overlap");
+    return TTT_OK;
+}
+
 LinearArgs linear_args(const ttt_linear_cfg *cfg, const Act &x, ttt_linear_state *st) {
     LinearArgs a{};
     a.q = TDesc{x.XQ.data, x.XQ.sB, x.XQ.sH, x.XQ.sL};
@@ -293,17 +325,71 @@ ttt_status ttt_linear_decode(const ttt_linear_cfg *cfg, int32_t T, ttt_tensor XQ
 
 ttt_status ttt_mlp_state_init(const ttt_mlp_cfg *cfg, const float *W1, const float *b1, const float *W2,
                               const float *b2, ttt_mlp_state *state, void *stream) {
-    if (!cfg) return fail(TTT_ERR_NULL, "cfg is NULL");
-    (void)W1; (void)b1; (void)W2; (void)b2; (void)state; (void)stream;
-    return fail(TTT_ERR_UNSUPPORTED, "TTT-MLP not built yet");
+    ttt_status s;
+    if ((s = check_mlp_cfg(cfg))) return s;
+    if (!W1 || !b1 || !W2 || !b2) return fail(TTT_ERR_NULL, "W1 / b1 / W2 / b2 is NULL");
+    std::vector<Range> sr;
+    if ((s = check_mlp_state(cfg, state, sr, false))) return s;
+    const int64_t H = cfg->H, D = cfg->D, F = cfg->F, n = (int64_t)cfg->B * H;
+    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e;
+    if ((e = launch_tile(state->W1, W1, H * D * F, n * D * F, hs)) != hipSuccess) return hip_fail(e, "tile W1");
+    if ((e = launch_tile(state->b1, b1, H * F, n * F, hs)) != hipSuccess) return hip_fail(e, "tile b1");
+    if ((e = launch_tile(state->W2, W2, H * F * D, n * F * D, hs)) != hipSuccess) return hip_fail(e, "tile W2");
+    if ((e = launch_tile(state->b2, b2, H * D, n * D, hs)) != hipSuccess) return hip_fail(e, "tile b2");
+    if ((e = launch_tile(state->W1_grad, nullptr, 1, n * D * F, hs)) != hipSuccess) return hip_fail(e, "zero W1_grad");
+    if ((e = launch_tile(state->b1_grad, nullptr, 1, n * F, hs)) != hipSuccess) return hip_fail(e, "zero b1_grad");
+    if ((e = launch_tile(state->W2_grad, nullptr, 1, n * F * D, hs)) != hipSuccess) return hip_fail(e, "zero W2_grad");
+    if ((e = launch_tile(state->b2_grad, nullptr, 1, n * D, hs)) != hipSuccess) return hip_fail(e, "zero b2_grad");
+    state->offset = 0;
+    return ok();
 }
 
 ttt_status ttt_mlp_prefill(const ttt_mlp_cfg *cfg, int32_t L, ttt_tensor XQ, ttt_tensor XK, ttt_tensor XV,
                            ttt_eta eta, const float *ln_w, const float *ln_b, ttt_mlp_state *state, ttt_tensor out,
                            void *stream) {
-    (void)cfg; (void)L; (void)XQ; (void)XK; (void)XV; (void)eta; (void)ln_w; (void)ln_b; (void)state; (void)out;
-    (void)stream;
-    return fail(TTT_ERR_UNSUPPORTED, "TTT-MLP not built yet");
+    ttt_status s;
+    if ((s = check_mlp_cfg(cfg))) return s;
+    if (L < 1) return fail(TTT_ERR_SHAPE, "token count %d must be >= 1", L);
+    std::vector<Range> sr;
+    if ((s = check_mlp_state(cfg, state, sr, true))) return s;
+    const Act x{XQ, XK, XV, out, eta, ln_w, ln_b};
+    if ((s = check_acts(x, cfg->B, cfg->H, L, cfg->D, cfg->in_dtype, cfg->out_dtype, sr))) return s;
+    if (state->offset % cfg->K != 0)
+        return fail(TTT_ERR_UNSUPPORTED, "TTT-MLP prefill needs offset %% K == 0 (offset %lld); continuing an open "
+                    "mini-batch is not implemented", (long long)state->offset);
+    MlpArgs a{};
+    a.q = TDesc{XQ.data, XQ.sB, XQ.sH, XQ.sL};
+    a.k = TDesc{XK.data, XK.sB, XK.sH, XK.sL};
+    a.v = TDesc{XV.data, XV.sB, XV.sH, XV.sL};
+    a.eta = eta.data;
+    a.eta_sB = eta.sB;
+    a.eta_sH = eta.sH;
+    a.ln_w = ln_w;
+    a.ln_b = ln_b;
+    a.W1 = state->W1;
+    a.b1 = state->b1;
+    a.W2 = state->W2;
+    a.b2 = state->b2;
+    a.W1g = state->W1_grad;
+    a.b1g = state->b1_grad;
+    a.W2g = state->W2_grad;
+    a.b2g = state->b2_grad;
+    a.out = ODesc{out.data, out.sB, out.sH, out.sL};
+    a.B = cfg->B;
+    a.H = cfg->H;
+    a.nblk = (L + cfg->K - 1) / cfg->K;
+    a.tail = L % cfg->K;
+    a.t0 = 0;
+    a.pos0 = state->offset;
+    a.rope = cfg->rope;
+    a.rope_base = cfg->rope_base;
+    a.eps = cfg->ln_eps;
+    hipError_t e = launch_mlp_dual(a, cfg->in_dtype == TTT_BF16, cfg->out_dtype == TTT_BF16,
+                                   reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "mlp kernel");
+    state->offset += L;
+    return ok();
 }
 
 }  // extern "C"

@@ -83,6 +83,53 @@ def oracle_linear(inp: dict, *, K=16, rope=False, chains=None, L=None):
     return np.stack(outs), np.stack(Ws), np.stack(bs), np.stack(Gs), np.stack(gbs)
 
 
+class MlpGPU:
+    """One TTT-MLP problem on the GPU: device inputs, state, out."""
+
+    def __init__(self, inp: dict, *, K=16, rope=False, out_dtype="f32", device="cuda"):
+        B, H, L, D = inp["XQ"].shape
+        F = inp["W1"].shape[-1]
+        self.B, self.H, self.L, self.D, self.F = B, H, L, D, F
+        self.cfg = libttt.mlp_cfg(B, H, F=F, K=K, in_dtype="bf16", out_dtype=out_dtype, rope=rope)
+        self.x = {n: inp[n].to(device).contiguous() for n in ("XQ", "XK", "XV")}
+        self.eta = inp["eta"].to(device)
+        self.ln_w, self.ln_b = inp["ln_w"].to(device).contiguous(), inp["ln_b"].to(device).contiguous()
+        odt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+        self.out = torch.full((B, H, L, D), float("nan"), dtype=odt, device=device)
+        self.state = libttt.MlpState.empty(B, H, D, F, device=device)
+        w = [inp[n].to(device).contiguous() for n in ("W1", "b1", "W2", "b2")]
+        libttt.ttt_mlp_state_init(self.cfg, *w, self.state)
+
+    def run(self, t0, t1):
+        sl = slice(t0, t1)
+        libttt.ttt_mlp_prefill(self.cfg, t1 - t0, self.x["XQ"][:, :, sl], self.x["XK"][:, :, sl],
+                               self.x["XV"][:, :, sl], self.eta[:, sl], self.ln_w, self.ln_b, self.state,
+                               self.out[:, :, sl])
+
+    def result(self):
+        torch.cuda.synchronize()
+        return (to_f64(self.out),) + tuple(to_f64(t) for t in self.state.tensors)
+
+
+def oracle_mlp(inp: dict, *, K=16, rope=False, chains=None, L=None):
+    """Oracle outputs and final state (W1, b1, W2, b2, G1, gb1, G2, gb2) for the
+    listed (b, h) chains (default all), each stacked over the chains."""
+    B, H, Lf, D = inp["XQ"].shape
+    F = inp["W1"].shape[-1]
+    L = Lf if L is None else L
+    chains = [(b, h) for b in range(B) for h in range(H)] if chains is None else chains
+    eta, lw, lb = to_f64(inp["eta"]), to_f64(inp["ln_w"]), to_f64(inp["ln_b"])
+    init = [to_f64(inp[n]) for n in ("W1", "b1", "W2", "b2")]
+    res = [[] for _ in range(9)]
+    for (b, h) in chains:
+        q, k, v = (to_f64(inp[n][b, h, :L]) for n in ("XQ", "XK", "XV"))
+        st = [a[h].copy() for a in init] + [np.zeros((D, F)), np.zeros(F), np.zeros((F, D)), np.zeros(D)]
+        o = oracle.mlp_chain(q, k, v, eta[h, :L], lw[h], lb[h], *st, K=K, rope=rope)
+        for i, a in enumerate([o] + st):
+            res[i].append(a)
+    return tuple(np.stack(r) for r in res)
+
+
 def max_abs(a, b) -> float:
     return float(np.max(np.abs(np.asarray(a) - np.asarray(b))))
 
@@ -93,5 +140,5 @@ def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
     return np.exp2(np.floor(np.log2(ax)) - 8)
 
 
-__all__ = ["LinearGPU", "oracle_linear", "max_abs", "tol_for", "make_inputs", "to_f64", "bf16_half_ulp",
+__all__ = ["LinearGPU", "oracle_linear", "MlpGPU", "oracle_mlp", "max_abs", "tol_for", "make_inputs", "to_f64", "bf16_half_ulp",
            "TOL_F32", "TOL_BF16"]

@@ -5,9 +5,15 @@ mini-batch 16), B = 4, L = 8192, bf16 inputs, fp32 state and output, seeded
 synthetic inputs resident in HBM.  One step = initialise the state from W0, b0
 and run the whole prefill over the batch (one pass of every step of the path).
 
-Prints one JSON line: throughput (tokens/s, a token = one position of one
-sequence over all heads), the roofline of the dominant kernel measured with
-HIP events on the launch stream, and the CPU oracle timed on a bounded sample.
+Other workloads (``--workload``):
+  linear_125m  TTT-Linear prefill, B = 8, H = 12, L = 2048, rotary on
+  mlp_350m     TTT-MLP prefill, B = 4, H = 16, L = 4096, hidden 256
+  decode_1b    B = 64, H = 32: prefill 512 tokens, then 256 single-token
+               decode calls; the value is decode tokens/s
+
+Prints one JSON line: whole-step throughput, the roofline of the dominant
+kernel (its launches timed with HIP events on the stream they run on), and
+the CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload linear_1b]
 """
@@ -24,14 +30,26 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 MFMA, TFLOP/s
+D, K, F = 64, 16, 256
 
-# algorithmic bytes per token-head of TTT-Linear prefill: q, k, v (bf16) +
-# eta (fp32) + out (fp32)
-LINEAR_BYTES_PER_TOKEN_HEAD = {("bf16", "f32"): 3 * 64 * 2 + 4 + 64 * 4, ("bf16", "bf16"): 3 * 64 * 2 + 4 + 64 * 2,
-                               ("f32", "f32"): 3 * 64 * 4 + 4 + 64 * 4}
-# state read + written once per chain: W, b (fp32)
-LINEAR_STATE_BYTES_PER_CHAIN = 2 * (64 * 64 + 64) * 4
+
+# algorithmic HBM bytes of one TTT-Linear token of one head: q, k, v in + eta
+# + out (prefill and decode alike)
+def linear_token_bytes(in_dtype, out_dtype):
+    e = {"bf16": 2, "f32": 4}
+    return 3 * D * e[in_dtype] + 4 + D * e[out_dtype]
+
+
+# the state a prefill chain reads once and writes once: W, b (fp32)
+LINEAR_STATE_BYTES = 2 * (D * D + D) * 4
+# the state of one TTT-MLP chain, read once and written once: W1, b1, W2, b2
+MLP_STATE_BYTES = 2 * (D * F + F + F * D + D) * 4
+# MFMA flops of one TTT-MLP mini-batch of one chain (dual form):
+#   X W1, Q W1, X2 W2, ng2 W2^T, Xb2 W2, X^T ng1, X2^T ng2   7 x 2*16*64*256
+#   Q X^T, M2 ng2                                              2 x 2*16*16*64
+#   M1 ng1, Xb2 X2^T                                           2 x 2*16*16*256
+MLP_FLOPS_PER_BLOCK = 7 * 2 * K * D * F + 2 * 2 * K * K * D + 2 * 2 * K * K * F
 
 
 def parse():
@@ -39,32 +57,209 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="linear_1b",
-                    choices=["linear_1b", "linear_125m", "mlp_350m", "decode_1b"])
+    ap.add_argument("--workload", default="linear_1b", choices=["linear_1b", "linear_125m", "mlp_350m", "decode_1b"])
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--rope", action="store_true", help="rotary on for a linear workload that has it off")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="after the run, copy a buffer of this many MiB twice (calibrates HBM byte counters)")
     return ap.parse_args()
 
 
-def cpu_baseline_linear(inp, w, rope):
-    """The oracle as it stands, on batch 0 (all heads, full L) of the workload,
-    OpenMP over the heads."""
+# ---------------------------------------------------------------------------
+# timing helpers
+# ---------------------------------------------------------------------------
+class Timer:
+    """HIP events around launches on one stream."""
+
+    def __init__(self, stream):
+        import torch
+
+        self.torch, self.stream, self.pairs = torch, stream, {}
+
+    def start(self, name):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        self.pairs.setdefault(name, []).append([e, None])
+
+    def stop(self, name):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        self.pairs[name][-1][1] = e
+
+    def ms(self, name):
+        return [a.elapsed_time(b) for a, b in self.pairs.get(name, [])]
+
+
+def stats(xs):
+    xs = sorted(xs)
+    q = lambda p: xs[min(len(xs) - 1, int(round(p * (len(xs) - 1))))]  # noqa: E731
+    return {"mean": sum(xs) / len(xs), "p10": q(0.1), "p50": q(0.5), "p90": q(0.9), "n": len(xs)}
+
+
+def run_steps(args, step):
+    import torch
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    runs, if they were taken on the kernel source as it is now."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh).get(f"{kernel}@{workload}")
+    from test_rnn_layers_amd.profile_summary import source_digest
+
+    if not rec or rec.get("source_sha256") != source_digest(kernel):
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+def roofline(kernel, workload, *, bound, amount, kernel_ms, per_unit, units):
+    peak, unit = (HBM_PEAK_GBS, "GB/s") if bound == "hbm" else (F16_MFMA_PEAK_TFLOPS, "TFLOP/s")
+    scale = 1e9 if bound == "hbm" else 1e12
+    achieved = amount / (kernel_ms["mean"] * 1e-3) / scale
+    return {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+            "traffic": measured_traffic(kernel, workload), "kernel": kernel, "kernel_ms": kernel_ms,
+            "algorithmic_per_launch": amount, "algorithmic_per_unit": per_unit, "units_per_launch": units}
+
+
+def copy_probe(mb):
+    """A plain device copy of known size (for scaling the byte counters)."""
+    import torch
+
+    n = mb * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copy probe: {n * 4} bytes read, {n * 4} bytes written per copy", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baselines (bounded samples)
+# ---------------------------------------------------------------------------
+def _f64(t):
+    return t.double().numpy()
+
+
+def cpu_linear(inp, w, rope, budget):
+    """The oracle over whole batch rows of the workload (all heads, full L,
+    OpenMP over the chains), cycling through the rows until the time budget
+    is spent."""
     import numpy as np
 
     import oracle
 
-    H, L, D = w.H, w.L, 64
-    f64 = lambda t: t.double().numpy()  # noqa: E731
-    XQ, XK, XV = (np.ascontiguousarray(f64(inp[n][:1])) for n in ("XQ", "XK", "XV"))
-    eta, lw, lb = f64(inp["eta"]), f64(inp["ln_w"]), f64(inp["ln_b"])
-    W = np.ascontiguousarray(np.broadcast_to(f64(inp["W0"]), (1, H, D, D)))
-    b = np.ascontiguousarray(np.broadcast_to(f64(inp["b0"]), (1, H, D)))
+    H, L = w.H, w.L
+    eta, lw, lb = _f64(inp["eta"]), _f64(inp["ln_w"]), _f64(inp["ln_b"])
+    x = {n: _f64(inp[n]) for n in ("XQ", "XK", "XV")}
+    done, dt = 0, 0.0
+    while done == 0 or dt < budget:
+        r = done % w.B
+        XQ, XK, XV = (np.ascontiguousarray(x[n][r:r + 1]) for n in ("XQ", "XK", "XV"))
+        W = np.ascontiguousarray(np.broadcast_to(_f64(inp["W0"]), (1, H, D, D)))
+        b = np.ascontiguousarray(np.broadcast_to(_f64(inp["b0"]), (1, H, D)))
+        t0 = time.perf_counter()
+        oracle.linear_batch(XQ, XK, XV, eta, 0, lw, lb, W, b, np.zeros_like(W), np.zeros_like(b), K=K, rope=rope)
+        dt += time.perf_counter() - t0
+        done += 1
+    return {"value": done * L / dt, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"{done} batch rows of the workload's {w.B}, cycled ({H} heads x {L} tokens each), "
+                      f"fp64 primal form, {dt:.1f} s"}
+
+
+def cpu_mlp(inp, w, budget):
+    import numpy as np
+
+    import oracle
+
+    H, L = w.H, w.L
+    eta, lw, lb = _f64(inp["eta"]), _f64(inp["ln_w"]), _f64(inp["ln_b"])
+    st0 = [_f64(inp[n]) for n in ("W1", "b1", "W2", "b2")]
+    x = {n: _f64(inp[n]) for n in ("XQ", "XK", "XV")}
+    done, dt = 0, 0.0
+    while done == 0 or dt < budget:
+        r = done % w.B
+        XQ, XK, XV = (np.ascontiguousarray(x[n][r:r + 1]) for n in ("XQ", "XK", "XV"))
+        st = [np.ascontiguousarray(a[None]) for a in st0]
+        grads = [np.zeros_like(a) for a in st]
+        t0 = time.perf_counter()
+        oracle.mlp_batch(XQ, XK, XV, eta, 0, lw, lb, *st, *grads, K=K)
+        dt += time.perf_counter() - t0
+        done += 1
+    return {"value": done * L / dt, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"{done} batch rows of the workload's {w.B}, cycled ({H} heads x {L} tokens each), "
+                      f"fp64 primal form, {dt:.1f} s"}
+
+
+def cpu_decode(inp, w, budget):
+    """The oracle's decode rate: every sequence prefilled over 512 tokens
+    (untimed), then its 256 decode tokens timed from a copy of that state,
+    repeated until the budget is spent."""
+    import numpy as np
+
+    import oracle
+
+    B, H, P, T = w.B, w.H, w.prefill, w.decode
+    eta, lw, lb = _f64(inp["eta"]), _f64(inp["ln_w"]), _f64(inp["ln_b"])
+    x = {n: _f64(inp[n]) for n in ("XQ", "XK", "XV")}
+    W = np.ascontiguousarray(np.broadcast_to(_f64(inp["W0"]), (B, H, D, D)))
+    b = np.ascontiguousarray(np.broadcast_to(_f64(inp["b0"]), (B, H, D)))
     G, gb = np.zeros_like(W), np.zeros_like(b)
-    t0 = time.perf_counter()
-    oracle.linear_batch(XQ, XK, XV, eta, 0, lw, lb, W, b, G, gb, K=16, rope=rope)
-    dt = time.perf_counter() - t0
-    return {"value": L / dt, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": f"batch row 0 of the workload: {H} heads x {L} tokens (fp64 primal form), {dt:.2f} s"}
+    sl = lambda n, a, z: np.ascontiguousarray(x[n][:, :, a:z])  # noqa: E731
+    oracle.linear_batch(sl("XQ", 0, P), sl("XK", 0, P), sl("XV", 0, P), np.ascontiguousarray(eta[:, :P]), 0, lw,
+                        lb, W, b, G, gb, K=K)
+    dq, dk, dv = sl("XQ", P, P + T), sl("XK", P, P + T), sl("XV", P, P + T)
+    de = np.ascontiguousarray(eta[:, P:P + T])
+    reps, dt = 0, 0.0
+    while reps == 0 or dt < budget:
+        s = [a.copy() for a in (W, b, G, gb)]
+        t0 = time.perf_counter()
+        oracle.linear_batch(dq, dk, dv, de, 0, lw, lb, *s, K=K, offset=P)
+        dt += time.perf_counter() - t0
+        reps += 1
+    return {"value": reps * B * T / dt, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"all {B} sequences x {H} heads, {T} decode tokens after a {P}-token prefill (prefill "
+                      f"untimed), {reps} repetitions, fp64 primal form, {dt:.1f} s"}
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+def common(args, w, value, elapsed, dtype, extra_cfg):
+    return {"metric": None, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / args.steps, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+            "data": "synthetic: seeded N(0,1) q/k/v rounded to bf16, W ~ N(0, 0.02^2), zero biases, "
+                    "eta = sigmoid(N(0,1))/64",
+            "config": dict({"workload": w.name, "B": w.B, "H": w.H, "head_dim": D, "mini_batch": K,
+                            "in_dtype": w.dtype, "out_dtype": args.out_dtype, "state_dtype": "f32",
+                            "parallelism": "single GPU, one workgroup per (batch, head) chain"}, **extra_cfg)}
+
+
+def input_sets(inp, dev):
+    """Two resident input sets, alternated between steps, so that the 256 MB
+    MALL does not serve one step's inputs from the previous step."""
+    sets = []
+    for s in range(2):
+        xs = {n: inp[n].to(dev).contiguous() for n in ("XQ", "XK", "XV")}
+        if s == 1:
+            xs = {n: t.flip(0).contiguous() for n, t in xs.items()}
+        sets.append(xs)
+    return sets
 
 
 def bench_linear(args, w):
@@ -74,77 +269,152 @@ def bench_linear(args, w):
     from test_rnn_layers_amd.synth import workload_inputs
 
     dev = "cuda"
-    B, H, L, D = w.B, w.H, w.L, 64
-    rope = w.rope
+    B, H, L = w.B, w.H, w.L
+    rope = w.rope or args.rope
     inp = workload_inputs(w)
     cfg = libttt.linear_cfg(B, H, in_dtype=w.dtype, out_dtype=args.out_dtype, rope=rope)
     odt = torch.float32 if args.out_dtype == "f32" else torch.bfloat16
-    # two resident input sets, alternated, so the 256 MB MALL does not serve
-    # the inputs of the step from the previous one
-    sets = []
-    for s in range(2):
-        xs = {n: inp[n].to(dev).contiguous() for n in ("XQ", "XK", "XV")}
-        if s == 1:
-            xs = {n: t.flip(0).contiguous() for n, t in xs.items()}
-        sets.append(xs)
+    sets = input_sets(inp, dev)
     eta = inp["eta"].to(dev).contiguous()
     lw, lb = inp["ln_w"].to(dev).contiguous(), inp["ln_b"].to(dev).contiguous()
     W0, b0 = inp["W0"].to(dev).contiguous(), inp["b0"].to(dev).contiguous()
     out = torch.empty((B, H, L, D), dtype=odt, device=dev)
     st = libttt.LinearState.empty(B, H, D, device=dev)
     stream = torch.cuda.current_stream()
-
-    ev = []
+    tm = Timer(stream)
 
     def step(i, timed):
         x = sets[i % 2]
         libttt.ttt_linear_state_init(cfg, W0, b0, st, stream)
         if timed:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
+            tm.start("prefill")
         libttt.ttt_linear_prefill(cfg, L, x["XQ"], x["XK"], x["XV"], eta, lw, lb, st, out, stream)
         if timed:
-            e1.record(stream)
-            ev.append((e0, e1))
+            tm.stop("prefill")
 
-    for i in range(args.warmup):
-        step(i, False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, True)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
-
-    tokens = B * L
-    per = LINEAR_BYTES_PER_TOKEN_HEAD[(w.dtype, args.out_dtype)]
-    alg_bytes = per * B * H * L + LINEAR_STATE_BYTES_PER_CHAIN * B * H
-    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
-    res = {
-        "metric": "TTT-Linear prefill tokens/sec (1B shape, L=8192) + % of HBM/MFMA roofline"
-        if w.name.startswith("linear_1b") else f"TTT-Linear prefill tokens/sec ({w.name})",
-        "value": tokens * args.steps / elapsed,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": elapsed * 1e3 / args.steps,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded N(0,1) q/k/v, W0 ~ N(0, 0.02^2), eta = sigmoid(N(0,1))/64)",
-        "config": {"workload": w.name, "B": B, "H": H, "head_dim": D, "L": L, "mini_batch": 16,
-                   "in_dtype": w.dtype, "out_dtype": args.out_dtype, "state_dtype": "f32", "rope": rope,
-                   "parallelism": "single GPU, one workgroup per (batch, head) chain"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "linear_dual_kernel", "kernel_ms": kern_ms,
-                     "algorithmic_bytes_per_launch": alg_bytes},
-    }
+    elapsed = run_steps(args, step)
+    per = linear_token_bytes(w.dtype, args.out_dtype)
+    amount = per * B * H * L + LINEAR_STATE_BYTES * B * H
+    res = common(args, w, B * L * args.steps / elapsed, elapsed, w.dtype, {"L": L, "rope": rope})
+    res["metric"] = ("TTT-Linear prefill tokens/sec (1B shape, L=8192) + % of HBM/MFMA roofline"
+                     if w.name.startswith("linear_1b") else f"TTT-Linear prefill tokens/sec ({w.name})")
+    res["roofline"] = roofline("linear_dual_kernel", w.name + ("_rope" if rope and not w.rope else ""),
+                               bound="hbm", amount=amount, kernel_ms=stats(tm.ms("prefill")),
+                               per_unit=f"{per} B per token-head + {LINEAR_STATE_BYTES} B state per chain",
+                               units=f"{B * H * L} token-heads, {B * H} chains")
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_linear(inp, w, rope)
+        res["cpu_baseline"] = cpu_linear(inp, w, rope, args.cpu_seconds)
+    return res
+
+
+def bench_mlp(args, w):
+    import torch
+
+    from test_rnn_layers_amd import libttt
+    from test_rnn_layers_amd.synth import workload_inputs
+
+    dev = "cuda"
+    B, H, L = w.B, w.H, w.L
+    inp = workload_inputs(w)
+    cfg = libttt.mlp_cfg(B, H, in_dtype=w.dtype, out_dtype=args.out_dtype)
+    odt = torch.float32 if args.out_dtype == "f32" else torch.bfloat16
+    sets = input_sets(inp, dev)
+    eta = inp["eta"].to(dev).contiguous()
+    lw, lb = inp["ln_w"].to(dev).contiguous(), inp["ln_b"].to(dev).contiguous()
+    init = [inp[n].to(dev).contiguous() for n in ("W1", "b1", "W2", "b2")]
+    out = torch.empty((B, H, L, D), dtype=odt, device=dev)
+    st = libttt.MlpState.empty(B, H, D, F, device=dev)
+    stream = torch.cuda.current_stream()
+    tm = Timer(stream)
+
+    def step(i, timed):
+        x = sets[i % 2]
+        libttt.ttt_mlp_state_init(cfg, *init, st, stream)
+        if timed:
+            tm.start("prefill")
+        libttt.ttt_mlp_prefill(cfg, L, x["XQ"], x["XK"], x["XV"], eta, lw, lb, st, out, stream)
+        if timed:
+            tm.stop("prefill")
+
+    elapsed = run_steps(args, step)
+    nblk = (L + K - 1) // K
+    amount = MLP_FLOPS_PER_BLOCK * B * H * nblk
+    res = common(args, w, B * L * args.steps / elapsed, elapsed, "bf16 in, fp16 MFMA operands, fp32 state",
+                 {"L": L, "mlp_hidden": F, "rope": False})
+    res["dtype"] = w.dtype
+    res["metric"] = f"TTT-MLP prefill tokens/sec ({w.name})"
+    res["roofline"] = roofline("mlp_dual_kernel", w.name, bound="mfma", amount=amount,
+                               kernel_ms=stats(tm.ms("prefill")),
+                               per_unit=f"{MLP_FLOPS_PER_BLOCK} MFMA flops per 16-token mini-batch per chain",
+                               units=f"{B * H * nblk} chain mini-batches")
+    hbm = linear_token_bytes(w.dtype, args.out_dtype) * B * H * L + MLP_STATE_BYTES * B * H
+    res["roofline"]["hbm_gbs"] = hbm / (res["roofline"]["kernel_ms"]["mean"] * 1e-3) / 1e9
+    res["roofline"]["note"] = ("64 chains on 256 CUs: one workgroup per chain, so at most a quarter of the "
+                               "chip's matrix cores can be busy")
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_mlp(inp, w, args.cpu_seconds)
+    return res
+
+
+def bench_decode(args, w):
+    import torch
+
+    from test_rnn_layers_amd import libttt
+    from test_rnn_layers_amd.synth import workload_inputs
+
+    dev = "cuda"
+    B, H, P, T = w.B, w.H, w.prefill, w.decode
+    inp = workload_inputs(w)
+    cfg = libttt.linear_cfg(B, H, in_dtype=w.dtype, out_dtype=args.out_dtype, rope=w.rope)
+    odt = torch.float32 if args.out_dtype == "f32" else torch.bfloat16
+    x = {n: inp[n].to(dev).contiguous() for n in ("XQ", "XK", "XV")}
+    eta = inp["eta"].to(dev).contiguous()
+    lw, lb = inp["ln_w"].to(dev).contiguous(), inp["ln_b"].to(dev).contiguous()
+    W0, b0 = inp["W0"].to(dev).contiguous(), inp["b0"].to(dev).contiguous()
+    out = torch.empty((B, H, P + T, D), dtype=odt, device=dev)
+    st = libttt.LinearState.empty(B, H, D, device=dev)
+    stream = torch.cuda.current_stream()
+    tm = Timer(stream)
+    # views of every decode token, made once
+    views = [tuple(x[n][:, :, t:t + 1] for n in ("XQ", "XK", "XV")) + (eta[:, t:t + 1], out[:, :, t:t + 1])
+             for t in range(P, P + T)]
+
+    def step(i, timed):
+        libttt.ttt_linear_state_init(cfg, W0, b0, st, stream)
+        if timed:
+            tm.start("prefill")
+        libttt.ttt_linear_prefill(cfg, P, x["XQ"][:, :, :P], x["XK"][:, :, :P], x["XV"][:, :, :P], eta[:, :P],
+                                  lw, lb, st, out[:, :, :P], stream)
+        if timed:
+            tm.stop("prefill")
+            tm.start("decode")
+        for j, (q, k, v, e, o) in enumerate(views):
+            if timed:
+                tm.start("token")
+            libttt.ttt_linear_decode(cfg, 1, q, k, v, e, lw, lb, st, o, stream)
+            if timed:
+                tm.stop("token")
+        if timed:
+            tm.stop("decode")
+
+    elapsed = run_steps(args, step)
+    dec = stats(tm.ms("decode"))
+    per_tok = linear_token_bytes(w.dtype, args.out_dtype)
+    # per chain and decode call: read W_s, b_s, G, gb; write G, gb; inputs/out
+    state_rw = 3 * (D * D + D) * 4
+    amount = (per_tok + state_rw) * B * H
+    res = common(args, w, B * T / (dec["mean"] * 1e-3), elapsed, w.dtype,
+                 {"prefill": P, "decode_steps": T, "rope": w.rope,
+                  "decode_phase_ms": dec, "prefill_ms": stats(tm.ms("prefill")),
+                  "value_is": "decode tokens/s over the 256 decode calls (GPU time incl. launch gaps)",
+                  "step_tokens_per_s": B * (P + T) * args.steps / elapsed})
+    res["metric"] = f"TTT-Linear decode tokens/sec ({w.name})"
+    res["roofline"] = roofline("linear_token_kernel", w.name, bound="hbm", amount=amount,
+                               kernel_ms=stats(tm.ms("token")),
+                               per_unit=f"{per_tok} B token in/out + {state_rw} B state read/write per chain",
+                               units=f"{B * H} chains, one token each")
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_decode(inp, w, args.cpu_seconds)
     return res
 
 
@@ -158,10 +428,10 @@ def main():
 
     w = {"linear_125m": WORKLOADS[1], "linear_1b": WORKLOADS[2], "mlp_350m": WORKLOADS[3],
          "decode_1b": WORKLOADS[4]}[args.workload]
-    if w.kind == "linear":
-        res = bench_linear(args, w)
-    else:
-        raise SystemExit(f"workload {args.workload} not wired yet")
+    fn = {"linear": bench_linear, "mlp": bench_mlp, "decode": bench_decode}[w.kind]
+    res = fn(args, w)
+    if args.copy_probe_mb:
+        copy_probe(args.copy_probe_mb)
     print(json.dumps(res), flush=True)
 
 

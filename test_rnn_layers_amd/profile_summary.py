@@ -1,0 +1,149 @@
+"""Turn rocprofv3 CSV output into the short text summaries kept with the
+sources, and the per-launch HBM traffic record that bench.py reports.
+
+    # kernel-trace statistics (rocprofv3 --kernel-trace --stats --output-format csv -d DIR ...)
+    python -m test_rnn_layers_amd.profile_summary stats DIR --kernel linear_dual_kernel \
+        --cmd "<the rocprofv3 command>" --out profiles/linear_dual_kernel_linear_1b.md
+
+    # HBM bytes: one --pmc FETCH_SIZE run and one --pmc WRITE_SIZE run of a
+    # bench command that ends with a plain copy of known size (--copy-probe-mb)
+    python -m test_rnn_layers_amd.profile_summary traffic --fetch DIR1 --write DIR2 \
+        --kernel linear_dual_kernel --workload linear_1b_B4_H32_L8192_bf16 --copy-mb 1024 \
+        --cmd "<the two rocprofv3 commands>" --out profiles/linear_dual_kernel_linear_1b_traffic.md
+
+The counters read KiB per dispatch; each is scaled by the ratio of the copy's
+known byte count to what the same counter read for the copy.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+KERNEL_SOURCES = {"linear_dual_kernel": "linear_dual.hip", "mlp_dual_kernel": "mlp_dual.hip",
+                  "linear_token_kernel": "linear_token.hip"}
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_digest(kernel: str) -> str:
+    """sha256 over the kernel's source file and the headers it includes."""
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "device_common.hpp", "launch.hpp"):
+        with open(os.path.join(PKG, "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _find(d: str, suffix: str) -> list[str]:
+    return sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+
+
+def _short(name: str, width: int = 90) -> str:
+    return name if len(name) <= width else name[: width - 3] + "..."
+
+
+def stats_summary(d: str, kernel: str, cmd: str) -> str:
+    files = _find(d, "kernel_stats.csv")
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    rows = list(csv.DictReader(open(files[0])))
+    lines = [f"# rocprofv3 kernel statistics: {kernel}", "", "Command:", "", "```", cmd, "```", "",
+             "| kernel | calls | avg (us) | min (us) | max (us) | total (ms) | % |", "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        mark = "**" if kernel in r["Name"] else ""
+        lines.append(f"| {mark}{_short(r['Name'])}{mark} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['TotalDurationNs']) / 1e6:.2f} | {float(r['Percentage']):.1f} |")
+    tr = _find(d, "kernel_trace.csv")
+    if tr:
+        dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+               for r in csv.DictReader(open(tr[0])) if kernel in r["Kernel_Name"]]
+        if dur:
+            lines += ["", f"{kernel}: {len(dur)} dispatches, median {statistics.median(dur):.1f} us, "
+                          f"mean {statistics.mean(dur):.1f} us"]
+    return "\n".join(lines) + "\n"
+
+
+def _counter(d: str, name: str) -> list[tuple[str, int, float]]:
+    """(kernel name, grid size, value) per dispatch of one counter."""
+    out = []
+    for f in _find(d, "counter_collection.csv"):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == name:
+                out.append((r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])))
+    return out
+
+
+def _copy_value(rows, copy_bytes: int) -> float:
+    """The counter for the copy probe: the last dispatches of a copy kernel
+    whose grid covers the probe buffer."""
+    vals = [v for (k, g, v) in rows if "copy" in k.lower() and g * 16 >= copy_bytes // 4]
+    if not vals:
+        raise SystemExit("copy probe dispatch not found")
+    return statistics.median(vals[-2:])
+
+
+def traffic_summary(fetch_dir, write_dir, kernel, workload, copy_mb, cmd):
+    copy_bytes = copy_mb << 20
+    fr, wr = _counter(fetch_dir, "FETCH_SIZE"), _counter(write_dir, "WRITE_SIZE")
+    kf = [v for (k, g, v) in fr if kernel in k]
+    kw = [v for (k, g, v) in wr if kernel in k]
+    if not kf or not kw:
+        raise SystemExit(f"no {kernel} dispatches with FETCH_SIZE / WRITE_SIZE")
+    cf, cw = _copy_value(fr, copy_bytes), _copy_value(wr, copy_bytes)
+    sf, sw = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    fb, wb = statistics.median(kf) * 1024 * sf, statistics.median(kw) * 1024 * sw
+    rec = {"source_sha256": source_digest(kernel), "fetch_bytes": fb, "write_bytes": wb,
+           "hbm_bytes_per_launch": fb + wb, "fetch_kib_raw": statistics.median(kf),
+           "write_kib_raw": statistics.median(kw), "copy_fetch_kib": cf, "copy_write_kib": cw,
+           "fetch_scale": sf, "write_scale": sw, "dispatches": [len(kf), len(kw)]}
+    db = json.load(open(TRAFFIC_JSON)) if os.path.exists(TRAFFIC_JSON) else {}
+    db[f"{kernel}@{workload}"] = rec
+    with open(TRAFFIC_JSON, "w") as fh:
+        json.dump(db, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    lines = [f"# HBM traffic of {kernel} ({workload})", "", "Commands:", "", "```", cmd, "```", "",
+             f"- copy probe: {copy_bytes} bytes read and written; FETCH_SIZE read {cf:.0f} KiB, WRITE_SIZE "
+             f"{cw:.0f} KiB -> scale {sf:.4f} (fetch), {sw:.4f} (write)",
+             f"- {kernel}: FETCH_SIZE {statistics.median(kf):.0f} KiB, WRITE_SIZE {statistics.median(kw):.0f} KiB "
+             f"per dispatch (median of {len(kf)} / {len(kw)})",
+             f"- scaled: {fb / 1e6:.1f} MB read + {wb / 1e6:.1f} MB written = {(fb + wb) / 1e6:.1f} MB per launch",
+             f"- kernel source sha256 {rec['source_sha256'][:16]}..."]
+    return "\n".join(lines) + "\n"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd_name", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("--kernel", required=True)
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--copy-mb", type=int, required=True)
+    t.add_argument("--cmd", required=True)
+    t.add_argument("--out", required=True)
+    a = ap.parse_args()
+    if a.cmd_name == "stats":
+        text = stats_summary(a.dir, a.kernel, a.cmd)
+    else:
+        text = traffic_summary(a.fetch, a.write, a.kernel, a.workload, a.copy_mb, a.cmd)
+    os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)
+    with open(a.out, "w") as fh:
+        fh.write(text)
+    print(text)
+
+
+if __name__ == "__main__":
+    main()

@@ -226,17 +226,18 @@ __device__ __forceinline__ float row_sum16(float x) {
 // value of lane (n + 8) mod 16 of the row (the lane holding columns +-32)
 __device__ __forceinline__ float row_swap8(float x) { return dpp<0x128>(x); }  // row_ror:8
 
+// workgroup barrier that the instruction scheduler cannot move work across
+// (s_barrier alone only orders memory operations): work placed between two
+// barriers runs in that phase
+__device__ __forceinline__ void phase_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---------------------------------------------------------------------------
 // row waves: inputs of one mini-batch for token row t, columns 4n .. 4n+3
 // ---------------------------------------------------------------------------
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-
-// buffer resource over `bytes` bytes at `base` (raw, stride 0)
-__device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
 
 template <typename Tin>
 struct Raw;
@@ -245,6 +246,9 @@ struct Raw<__bf16> {
     uint2 q, k, v;  // 4 bf16 each
     float eta;
     using U = uint2;
+    __device__ static void pin(Raw &r) {
+        asm volatile("" : "+v"(r.q.x), "+v"(r.q.y), "+v"(r.k.x), "+v"(r.k.y), "+v"(r.v.x), "+v"(r.v.y), "+v"(r.eta));
+    }
     __device__ static void unpack(uint2 u, float (&x)[4]) {
         x[0] = __builtin_bit_cast(float, u.x << 16);
         x[1] = __builtin_bit_cast(float, u.x & 0xffff0000u);
@@ -257,6 +261,10 @@ struct Raw<float> {
     uint4 q, k, v;
     float eta;
     using U = uint4;
+    __device__ static void pin(Raw &r) {
+        asm volatile("" : "+v"(r.q.x), "+v"(r.q.y), "+v"(r.q.z), "+v"(r.q.w), "+v"(r.k.x), "+v"(r.k.y), "+v"(r.k.z),
+                     "+v"(r.k.w), "+v"(r.v.x), "+v"(r.v.y), "+v"(r.v.z), "+v"(r.v.w), "+v"(r.eta));
+    }
     __device__ static void unpack(uint4 u, float (&x)[4]) {
         x[0] = __builtin_bit_cast(float, u.x);
         x[1] = __builtin_bit_cast(float, u.y);
@@ -265,41 +273,70 @@ struct Raw<float> {
     }
 };
 
-// what the LayerNorm phases need of one mini-batch, per lane; the token's
-// learning rate is folded in: u' = eta * gamma * (LN(z) - (v - k)) = eg2 * xhat + cel
+// what the LayerNorm phases need of one mini-batch, per lane
 struct RowRegs {
-    float cel[4];   // eta * gamma * (beta - v + k)
-    float eg2[4];   // eta * gamma^2
+    float cel[4];   // gamma * (k - v + beta): the target term of u = gamma * (LN(z) - (v - k))
     float qres[4];  // q + beta
+    float eta;      // learning rate of the token
 };
+
+// sums over the 16 lanes of the row of two values (interleaved chains)
+__device__ __forceinline__ void row_sum16x2(float &x, float &y) {
+    x += dpp<0xB1>(x);
+    y += dpp<0xB1>(y);
+    x += dpp<0x4E>(x);
+    y += dpp<0x4E>(y);
+    x += dpp<0x141>(x);
+    y += dpp<0x141>(y);
+    x += dpp<0x140>(x);
+    y += dpp<0x140>(y);
+}
 
 template <typename Tin, typename Tout, typename T, bool ROPE>
 struct RowWave {
     const LinearArgs &a;
     int t, n, rw;  // token row 4rw + g, lane n within the row
     int N;
-    // per-lane pointers at token row t, column 4n of the first mini-batch of
-    // the call, and elements per mini-batch; the output goes through a
-    // buffer resource (byte offset of the lane, bytes per mini-batch)
-    const Tin *pq, *pk, *pv;
-    const float *pe;
-    int64_t sq, sk, sv;
-    Rsrc ro;
-    uint32_t oo, bo;
+    // inputs: wave-uniform byte pointers to the next mini-batch to fetch
+    // (advanced by one mini-batch per fetch), bytes per mini-batch, and this
+    // lane's byte offsets within a mini-batch (32-bit: the host bounds them)
+    const char *fq, *fk, *fv, *fe;
+    int64_t bq, bk, bv;
+    uint32_t oq, ok, ov, oe;
+    int nf;  // next mini-batch to fetch
+    // output: wave-uniform byte pointer of mini-batch 0, bytes per
+    // mini-batch, this lane's byte offset.  A global store: the compiler
+    // separates a wide global store from a later write of its data registers
+    // (it does not do so for a buffer store with a register soffset, and on
+    // this chip such a write right after the store corrupts the stored data)
+    char *fo;
+    int64_t bo;
+    uint32_t oo;
     float gam[4], gam2[4], bet[4], gb[4];
     float cs[4], sn[4];    // rotary cos and signed sin of columns 4n + e at position t
 
-    __device__ void fetch(Raw<Tin> &r, int blk) const {
-        blk = blk < N ? blk : N - 1;  // past the end: a harmless in-bounds re-read
+    // mini-batches are fetched in order; the pointers stop at the last one,
+    // so fetches past the end re-read it (in bounds, never staged for use)
+    __device__ void fetch(Raw<Tin> &r) {
         using U = typename Raw<Tin>::U;
-        r.q = *(const U *)(pq + (int64_t)blk * sq);  // blk * s*: wave-uniform
-        r.k = *(const U *)(pk + (int64_t)blk * sk);
-        r.v = *(const U *)(pv + (int64_t)blk * sv);
-        r.eta = pe[(int64_t)blk * kM];
+        r.q = *(const U *)(fq + oq);
+        r.k = *(const U *)(fk + ok);
+        r.v = *(const U *)(fv + ov);
+        r.eta = *(const float *)(fe + oe);
+        const bool adv = ++nf < N;
+        fq += adv ? bq : 0;
+        fk += adv ? bk : 0;
+        fv += adv ? bv : 0;
+        fe += adv ? (int64_t)(kM * sizeof(float)) : 0;
     }
 
     // rotary, MFMA row fragments of q and k into LDS, LayerNorm operands into rr
-    __device__ void stage(Stage<T> &S, const Raw<Tin> &r, RowRegs &rr) const {
+    __device__ void stage(Stage<T> &S, const Raw<Tin> &in, RowRegs &rr) const {
+        // the inputs are consumed here and not earlier: the empty asm reads and
+        // redefines them, so the conversions below (and the wait for the loads
+        // they need) cannot be scheduled ahead of this mini-batch
+        Raw<Tin> r = in;
+        Raw<Tin>::pin(r);
         float qv[4], kv[4], vv[4];
         Raw<Tin>::unpack(r.q, qv);
         Raw<Tin>::unpack(r.k, kv);
@@ -316,61 +353,62 @@ struct RowWave {
         Op<T>::put4(&S.kx[t][4 * n], kv[0], kv[1], kv[2], kv[3]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            rr.cel[e] = r.eta * (gam[e] * (kv[e] - vv[e]) + gb[e]);
-            rr.eg2[e] = r.eta * gam2[e];
+            rr.cel[e] = fmaf(gam[e], kv[e] - vv[e], gb[e]);
             rr.qres[e] = qv[e] + bet[e];
         }
+        rr.eta = r.eta;
     }
 
-    // LayerNorm backward of Z_nb (row t): ng = -eta * dL/dZ, to the ng tile
+    // LayerNorm backward of Z_nb (row t) into the ng tile:
+    //   u = gamma * (LN(z) - (v - k)) = gamma^2 xhat + cel
+    //   ng = -eta * dL/dz = -eta * rs * (u - mean(u) - xhat * mean(u xhat))
+    // Mean and mean square share one reduction round, as do the two means
+    // of u (short dependency chains: this is on the sequential path).
     __device__ void ln_backward(Smem<T> &sm, const RowRegs &rr) const {
         const f32x4 z = *(const f32x4 *)&sm.zbuf[t][4 * n];
-        const float mu = row_sum16(z[0] + z[1] + z[2] + z[3]) * (1.f / kD);
-        float d[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) d[e] = z[e] - mu;
-        const float var = row_sum16(d[0] * d[0] + d[1] * d[1] + d[2] * d[2] + d[3] * d[3]) * (1.f / kD);
+        float s1 = (z[0] + z[1]) + (z[2] + z[3]);
+        float s2 = fmaf(z[0], z[0], z[1] * z[1]) + fmaf(z[2], z[2], z[3] * z[3]);
+        row_sum16x2(s1, s2);
+        const float mu = s1 * (1.f / kD);
+        const float var = fmaxf(fmaf(-mu, mu, s2 * (1.f / kD)), 0.f);
         const float rs = __builtin_amdgcn_rsqf(var + a.eps);  // var + eps >= eps > 0
-        float xh[4], u[4], su = 0.f, sux = 0.f;
+        const float mrs = -mu * rs;
+        float xh[4], u[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            xh[e] = d[e] * rs;
-            u[e] = rr.eg2[e] * xh[e] + rr.cel[e];  // eta * gamma * (LN(z) - (v - k))
-            su += u[e];
-            sux += u[e] * xh[e];
+            xh[e] = fmaf(z[e], rs, mrs);
+            u[e] = fmaf(gam2[e], xh[e], rr.cel[e]);
         }
-        su = row_sum16(su) * (1.f / kD);
-        sux = row_sum16(sux) * (1.f / kD);
-        // ng = -rs * (u - mean(u) - xh * mean(u xh))
-        const float A = -rs;
-        const float C0 = rs * su, C1 = rs * sux;
+        float su = (u[0] + u[1]) + (u[2] + u[3]);
+        float sux = fmaf(u[0], xh[0], u[1] * xh[1]) + fmaf(u[2], xh[2], u[3] * xh[3]);
+        row_sum16x2(su, sux);
+        const float A = -rr.eta * rs;
+        const float C0 = -A * su * (1.f / kD), C1 = -A * sux * (1.f / kD);
         float ng[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ng[e] = u[e] * A + (xh[e] * C1 + C0);
+        for (int e = 0; e < 4; ++e) ng[e] = fmaf(u[e], A, fmaf(xh[e], C1, C0));
         Op<T>::put4(&sm.gm[t][4 * n], ng[0], ng[1], ng[2], ng[3]);
     }
 
     // LayerNorm forward of Zbar_nb (row t): out = q + LN(Zbar)
     __device__ void ln_forward(const Smem<T> &sm, const RowRegs &rr, int nb) const {
         const f32x4 zb = *(const f32x4 *)&sm.zbbuf[nb & 1][t][4 * n];
-        const float mu = row_sum16(zb[0] + zb[1] + zb[2] + zb[3]) * (1.f / kD);
-        float d[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) d[e] = zb[e] - mu;
-        const float var = row_sum16(d[0] * d[0] + d[1] * d[1] + d[2] * d[2] + d[3] * d[3]) * (1.f / kD);
+        float s1 = (zb[0] + zb[1]) + (zb[2] + zb[3]);
+        float s2 = fmaf(zb[0], zb[0], zb[1] * zb[1]) + fmaf(zb[2], zb[2], zb[3] * zb[3]);
+        row_sum16x2(s1, s2);
+        const float mu = s1 * (1.f / kD);
+        const float var = fmaxf(fmaf(-mu, mu, s2 * (1.f / kD)), 0.f);
         const float rs = __builtin_amdgcn_rsqf(var + a.eps);  // var + eps >= eps > 0
+        const float mrs = -mu * rs;
         float y[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = d[e] * (rs * gam[e]) + rr.qres[e];
-        const uint32_t so = (uint32_t)nb * bo;
+        for (int e = 0; e < 4; ++e) y[e] = fmaf(fmaf(zb[e], rs, mrs), gam[e], rr.qres[e]);
+        char *o = fo + (int64_t)nb * bo + oo;
         if constexpr (std::is_same<Tout, float>::value) {
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{y[0], y[1], y[2], y[3]}), ro, (int)oo,
-                                                   (int)so, 0);
+            *(f32x4 *)o = f32x4{y[0], y[1], y[2], y[3]};
         } else {
             typedef __bf16 b4 __attribute__((ext_vector_type(4)));
-            __builtin_amdgcn_raw_buffer_store_b64(
-                __builtin_bit_cast(u32x2, b4{(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]}), ro, (int)oo,
-                (int)so, 0);
+            *(b4 *)o = b4{(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
         }
     }
 };
@@ -383,18 +421,23 @@ __device__ void row_main(const LinearArgs &a, Smem<T> &sm, int bi, int hi, int r
     R.rw = rw;
     R.N = a.ntok;
     const int N = a.ntok;
-    R.pq = (const Tin *)a.q.p + bi * a.q.sB + hi * a.q.sH + (int64_t)(a.t0 + R.t) * a.q.sL + 4 * n;
-    R.pk = (const Tin *)a.k.p + bi * a.k.sB + hi * a.k.sH + (int64_t)(a.t0 + R.t) * a.k.sL + 4 * n;
-    R.pv = (const Tin *)a.v.p + bi * a.v.sB + hi * a.v.sH + (int64_t)(a.t0 + R.t) * a.v.sL + 4 * n;
-    R.pe = a.eta + bi * a.eta_sB + hi * a.eta_sH + a.t0 + R.t;
-    R.sq = kM * a.q.sL;
-    R.sk = kM * a.k.sL;
-    R.sv = kM * a.v.sL;
-    // output rows of this chain from the first token of the call; the host
-    // checks that they span less than 2^31 bytes
-    R.ro = make_rsrc((Tout *)a.out.p + bi * a.out.sB + hi * a.out.sH + (int64_t)a.t0 * a.out.sL, 0x7fffffffu);
+    constexpr int64_t ein = sizeof(Tin);
+    R.fq = (const char *)((const Tin *)a.q.p + bi * a.q.sB + hi * a.q.sH + (int64_t)a.t0 * a.q.sL);
+    R.fk = (const char *)((const Tin *)a.k.p + bi * a.k.sB + hi * a.k.sH + (int64_t)a.t0 * a.k.sL);
+    R.fv = (const char *)((const Tin *)a.v.p + bi * a.v.sB + hi * a.v.sH + (int64_t)a.t0 * a.v.sL);
+    R.fe = (const char *)(a.eta + bi * a.eta_sB + hi * a.eta_sH + a.t0);
+    R.bq = kM * a.q.sL * ein;
+    R.bk = kM * a.k.sL * ein;
+    R.bv = kM * a.v.sL * ein;
+    R.oq = (uint32_t)((R.t * a.q.sL + 4 * n) * ein);
+    R.ok = (uint32_t)((R.t * a.k.sL + 4 * n) * ein);
+    R.ov = (uint32_t)((R.t * a.v.sL + 4 * n) * ein);
+    R.oe = (uint32_t)(R.t * sizeof(float));
+    R.nf = 0;
+    // output rows of this chain from the first token of the call
+    R.fo = (char *)((Tout *)a.out.p + bi * a.out.sB + hi * a.out.sH + (int64_t)a.t0 * a.out.sL);
     R.oo = (uint32_t)((R.t * a.out.sL + 4 * n) * (int64_t)sizeof(Tout));
-    R.bo = (uint32_t)(kM * a.out.sL * (int64_t)sizeof(Tout));
+    R.bo = kM * a.out.sL * (int64_t)sizeof(Tout);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int c = 4 * n + e;
@@ -412,21 +455,22 @@ __device__ void row_main(const LinearArgs &a, Smem<T> &sm, int bi, int hi, int r
     Raw<Tin> pf[kRing];  // pf[m % 4]: inputs of mini-batch m, fetched 4 steps ahead
     RowRegs rr[kRing];   // rr[m % 4]: LayerNorm operands of mini-batch m
 #pragma unroll
-    for (int i = 0; i < kRing; ++i) R.fetch(pf[i], i);
+    for (int i = 0; i < kRing; ++i) R.fetch(pf[i]);  // 0 .. 3
     R.stage(sm.st[0], pf[0], rr[0]);
-    R.fetch(pf[0], 4);
+    R.fetch(pf[0]);  // 4
     R.stage(sm.st[1], pf[1], rr[1]);
-    R.fetch(pf[1], 5);
-    __syncthreads();  // mini-batches 0, 1 staged
+    R.fetch(pf[1]);  // 5
+    phase_barrier();  // mini-batches 0, 1 staged
     R.stage(sm.st[2], pf[2], rr[2]);
-    R.fetch(pf[2], 6);
-    __syncthreads();  // Z_0 written
+    R.fetch(pf[2]);  // 6
+    phase_barrier();  // Z_0 written
     R.ln_backward(sm, rr[0]);
-    __syncthreads();  // ng_0 ready
+    phase_barrier();  // ng_0 ready
 
     // step m (1 <= m < N).  Phase 1 (off the sequential chain, while the
     // column waves form Z_m): forward LayerNorm of Zbar_m-2, stage m+2, fetch
-    // m+6.  Phase 2: backward LayerNorm of Z_m -> ng_m.
+    // m+6.  Phase 2: backward LayerNorm of Z_m -> ng_m (the column waves form
+    // Zbar_m-1 and the products of mini-batch m meanwhile).
     // In the loop m = 2 + 4k + i, so every register-set index is static:
     // slot (m+2) % 4 = (m-2) % 4 = i, slot m % 4 = (2+i) % 4.
     auto step = [&](int m, auto I) {
@@ -438,16 +482,16 @@ __device__ void row_main(const LinearArgs &a, Smem<T> &sm, int bi, int hi, int r
         // consume the register set before refilling it, so the refill lands in
         // the same registers (no copies that would wait on the new loads)
         __builtin_amdgcn_sched_barrier(0);
-        R.fetch(pf[i], m + 6);
-        __syncthreads();  // Z_m, Zbar_m-1 written
+        R.fetch(pf[i]);  // m + 6
+        phase_barrier();  // Z_m written
         R.ln_backward(sm, rr[(2 + i) % kRing]);
-        __syncthreads();  // ng_m ready
+        phase_barrier();  // ng_m ready, Zbar_m-1 written
     };
     // after the last step, with N = m + r (m = 2 mod 4): Zbar_N-2, Zbar_N-1
     auto last = [&](auto I) {
         constexpr int r = decltype(I)::value;
         R.ln_forward(sm, rr[r % kRing], N - 2);
-        __syncthreads();  // Zbar_N-1 written
+        phase_barrier();  // Zbar_N-1 written
         R.ln_forward(sm, rr[(r + 1) % kRing], N - 1);
     };
     using I0 = std::integral_constant<int, 0>;
@@ -455,17 +499,17 @@ __device__ void row_main(const LinearArgs &a, Smem<T> &sm, int bi, int hi, int r
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
     if (N == 1) {
-        __syncthreads();  // Zbar_0 written
+        phase_barrier();  // Zbar_0 written
         R.ln_forward(sm, rr[0], 0);
         return;
     }
     // step 1 (nothing to forward yet)
     R.stage(sm.st[3], pf[3], rr[3]);
     __builtin_amdgcn_sched_barrier(0);
-    R.fetch(pf[3], 7);
-    __syncthreads();  // Z_1, Zbar_0 written
+    R.fetch(pf[3]);  // 7
+    phase_barrier();  // Z_1 written
     R.ln_backward(sm, rr[1]);
-    __syncthreads();  // ng_1 ready
+    phase_barrier();  // ng_1 ready, Zbar_0 written
     int m = 2;
     for (; m + 3 < N; m += kRing) {  // branch-free steady state
         step(m, I0{});
@@ -530,7 +574,7 @@ __device__ void col_main(const LinearArgs &a, Smem<T> &sm, int ch, int c, int g,
     F4 kt[4];     // K_m^T rows 16r .. 16r+15 (A fragments)
     XF kxn;       // K_m row fragment
 
-    __syncthreads();  // mini-batches 0, 1 staged
+    phase_barrier();  // mini-batches 0, 1 staged
     {
         const XF wf = O::cvt_w(Wt);
         const XF kx0 = O::load_x(&sm.st[0].kx[0][0], n, g);
@@ -546,22 +590,24 @@ __device__ void col_main(const LinearArgs &a, Smem<T> &sm, int ch, int c, int g,
         O::kt_frags(kx0, sel, kt);
         kxn = kx1;
     }
-    __syncthreads();  // Z_0 written
-    __syncthreads();  // ng_0 ready
+    phase_barrier();  // Z_0 written
+    phase_barrier();  // ng_0 ready
 
     for (int m = 1; m < N; ++m) {
-        // phase 1, the sequential chain: Z_m = Y_m + C_m-1 ng_m-1, and Zbar_m-1
+        // phase 1, the sequential chain: Z_m = Y_m + C_m-1 ng_m-1
         const F4 gf = O::load_b(&sm.gm[0][0], 16 * c + n, g);
         const f32x4 Z = O::mma16(Cf, gf, Y);
 #pragma unroll
         for (int j = 0; j < 4; ++j) sm.zbuf[4 * g + j][16 * c + n] = Z[j];
-        const f32x4 ZB = O::mma16(Mf, gf, P);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sm.zbbuf[(m - 1) & 1][4 * g + j][16 * c + n] = ZB[j];
-        __syncthreads();  // Z_m, Zbar_m-1 written
+        phase_barrier();  // Z_m written
 
-        // phase 2 (row waves run the LayerNorm of Z_m): W_m, b_m, then the
-        // products of mini-batch m with W_m
+        // phase 2 (row waves run the LayerNorm of Z_m): Zbar_m-1, W_m, b_m,
+        // then the products of mini-batch m with W_m
+        {
+            const f32x4 ZB = O::mma16(Mf, gf, P);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sm.zbbuf[(m - 1) & 1][4 * g + j][16 * c + n] = ZB[j];
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) Wt[r] = O::mma16(kt[r], gf, Wt[r]);
         Bt = O::mma16(ones, gf, Bt);
@@ -574,14 +620,14 @@ __device__ void col_main(const LinearArgs &a, Smem<T> &sm, int ch, int c, int g,
         Cf = O::make(O::xx(kxn, kx1, one));
         O::kt_frags(kxn, sel, kt);
         kxn = kx1;
-        __syncthreads();  // ng_m ready
+        phase_barrier();  // ng_m ready, Zbar_m-1 written
     }
     {
         const F4 gf = O::load_b(&sm.gm[0][0], 16 * c + n, g);
         const f32x4 ZB = O::mma16(Mf, gf, P);
 #pragma unroll
         for (int j = 0; j < 4; ++j) sm.zbbuf[(N - 1) & 1][4 * g + j][16 * c + n] = ZB[j];
-        __syncthreads();  // Zbar_N-1 written
+        phase_barrier();  // Zbar_N-1 written
 #pragma unroll
         for (int r = 0; r < 4; ++r) Wt[r] = O::mma16(kt[r], gf, Wt[r]);
         Bt = O::mma16(ones, gf, Bt);

@@ -246,8 +246,9 @@ ttt_status linear_call(Mode mode, const ttt_linear_cfg *cfg, int32_t L, const Ac
         a.ntok = body;
         a.t0 = head;
         a.pos0 = st->offset + head;
-        // the dual kernel addresses each chain's rows with 32-bit byte offsets
-        const int64_t rows = (int64_t)body * K;
+        // the dual kernel addresses the rows of one mini-batch with 32-bit
+        // byte offsets from a per-mini-batch base
+        const int64_t rows = K;
         const size_t ei = dtype_size(cfg->in_dtype), eo = dtype_size(cfg->out_dtype);
         const int64_t span = std::max({(rows - 1) * x.XQ.sL * (int64_t)ei, (rows - 1) * x.XK.sL * (int64_t)ei,
                                        (rows - 1) * x.XV.sL * (int64_t)ei, (rows - 1) * x.out.sL * (int64_t)eo}) +

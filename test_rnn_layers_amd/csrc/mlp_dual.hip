@@ -24,7 +24,7 @@
 //    updates; X2, Xb2 and ng2 go through LDS where a row layout is needed;
 //  * Z2 and Zb2 are sums over the 8 hidden slices: partial tiles in LDS,
 //    summed by the LayerNorm waves 0..3 (16 lanes per token row, DPP sums);
-//  * operands are fp16 (bf16 inputs), accumulation fp32; GELU is exact (erf).
+//  * operands are fp16 (bf16 inputs), accumulation fp32; GELU in the erf form.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -98,10 +98,45 @@ __device__ __forceinline__ float row_sum16(float x) {
     return x;
 }
 
-// exact GELU and its derivative
-__device__ __forceinline__ float gelu(float x) { return 0.5f * x * (1.f + erff(x * 0.70710678118654752f)); }
-__device__ __forceinline__ float gelu_grad(float x) {
-    return 0.5f * (1.f + erff(x * 0.70710678118654752f)) + x * 0.39894228040143268f * expf(-0.5f * x * x);
+// GELU(x) = x Phi(x) and GELU'(x) = Phi(x) + x phi(x) with the erf form of
+// the normal CDF Phi.  erf comes from the rational approximation of
+// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26
+// (absolute error <= 1.5e-7 over the real line): for z >= 0
+//   erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2),
+//   t = 1 / (1 + p z).
+// With z = |x| / sqrt(2), exp(-z^2) = exp(-x^2 / 2) is also the factor of
+// the normal density phi, so GELU and GELU' share one exponential.
+struct Gelu {
+    float g, dg;
+};
+__device__ __forceinline__ float ncdf_tail(float x, float &e) {
+    // returns h = (1 - erf(|x| / sqrt(2))) / 2, and e = exp(-x^2 / 2)
+    constexpr float p = 0.3275911f, a1 = 0.254829592f, a2 = -0.284496736f, a3 = 1.421413741f,
+                    a4 = -1.453152027f, a5 = 1.061405429f;
+    const float z = fabsf(x) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(p, z, 1.f));
+    const float poly = t * fmaf(fmaf(fmaf(fmaf(a5, t, a4), t, a3), t, a2), t, a1);
+    e = __expf(-0.5f * x * x);
+    return 0.5f * poly * e;
+}
+__device__ __forceinline__ float gelu(float x) {
+    float e;
+    const float h = ncdf_tail(x, e);
+    return x * (x >= 0.f ? 1.f - h : h);
+}
+__device__ __forceinline__ Gelu gelu_both(float x) {
+    float e;
+    const float h = ncdf_tail(x, e);
+    const float cdf = x >= 0.f ? 1.f - h : h;
+    return Gelu{x * cdf, fmaf(x * 0.39894228040143268f, e, cdf)};  // phi(x) = e / sqrt(2 pi)
+}
+
+// workgroup barrier that the instruction scheduler cannot move work across
+// (s_barrier alone only orders memory operations)
+__device__ __forceinline__ void phase_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 template <typename Tin, typename Tout, bool ROPE>
@@ -218,7 +253,7 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
 
     In pre;
     if (lnw) fetch(pre, 0);
-    __syncthreads();  // constants in LDS
+    phase_barrier();  // constants in LDS
     if (lnw) {
         stage(pre, 0);
         if (NB > 1) fetch(pre, 1);
@@ -232,7 +267,7 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
             sel[h][i] = (i / 4 == h && 4 * g + (i & 3) == n) ? (_Float16)1.f : (_Float16)0.f;
     const h4 ones = h4{(_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f};
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    __syncthreads();
+    phase_barrier();
 
     // operands of the last step, kept for an open last mini-batch
     h4 kt[4], n1k[2], x2h[2], G2[4];
@@ -251,8 +286,9 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
             P1[s] = mfma32(qp1, wb1, mfma32(qp0, wb0, b1t[s]));
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                X2[s][j] = gelu(z1[j]);
-                D1[s][j] = gelu_grad(z1[j]);
+                const Gelu gg = gelu_both(z1[j]);
+                X2[s][j] = gg.g;
+                D1[s][j] = gg.dg;
                 sm.x2[4 * g + j][32 * w + 16 * s + n] = (_Float16)X2[s][j];
             }
         }
@@ -273,7 +309,7 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) kt[r] = to_h4(mfma32(r < 2 ? xp0 : xp1, sel[r & 1], zero));
         if (nb > 0 && threadIdx.x < kD) sm.b2[threadIdx.x] = sm.b2n[threadIdx.x];  // previous step
-        __syncthreads();  // B1: X2 in LDS, b2 current
+        phase_barrier();  // B1: X2 in LDS, b2 current
 
         // ---- P1: partial Z2 over this hidden slice ----
         const h8 x2p = row_perm(&sm.x2[0][0], HP, n, g, 32 * w);
@@ -283,7 +319,7 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) sm.part[w][4 * g + j][16 * r + n] = z2[j];
         }
-        __syncthreads();  // B2
+        phase_barrier();  // B2
 
         // ---- P2: Z2 = sum of slices + b2; LayerNorm backward -> ng2 ----
         if (lnw) {
@@ -311,7 +347,7 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
             for (int e = 0; e < 4; ++e) ng[e] = -rs * (u[e] - su - xh[e] * sux);
             *(h4 *)&sm.ng2[t][4 * n] = h4{(_Float16)ng[0], (_Float16)ng[1], (_Float16)ng[2], (_Float16)ng[3]};
         }
-        __syncthreads();  // B3: ng2 in LDS
+        phase_barrier();  // B3: ng2 in LDS
 
         // ---- P3: ng1, Zb1, Xb2; step of W1, b1, b2 ----
         const h8 gp0 = row_perm(&sm.ng2[0][0], NP, n, g, 0), gp1 = row_perm(&sm.ng2[0][0], NP, n, g, 32);
@@ -347,7 +383,7 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
                 if (g == 0) sm.b2n[16 * r + n] = bn[0];
             }
         }
-        __syncthreads();  // B4: Xb2 in LDS
+        phase_barrier();  // B4: Xb2 in LDS
 
         // ---- P4: partial Zb2 over this hidden slice; the causal term ----
         {
@@ -383,7 +419,7 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
                 for (int j = 0; j < 4; ++j) sm.part[8][4 * g + j][16 * r + n] = z[j];
             }
         }
-        __syncthreads();  // B5
+        phase_barrier();  // B5
 
         // ---- P5: Zb2, out = q + LN(Zb2); stage the next mini-batch ----
         if (lnw) {
@@ -415,7 +451,7 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
                 if (nb + 2 < NB) fetch(pre, nb + 2);
             }
         }
-        __syncthreads();  // next mini-batch staged; part, x2, xb2, ng2 free
+        phase_barrier();  // next mini-batch staged; part, x2, xb2, ng2 free
     }
 
     // ---- final state (an open last mini-batch left W, b at its start) ----

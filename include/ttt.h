@@ -39,7 +39,8 @@
  *  - between mini-batch boundaries the state holds the mini-batch-start W, b
  *    plus the accumulated eta-weighted gradients (the pages' W1_grad,
  *    b1_grad); they are committed and cleared at every boundary;
- *  - TTT-MLP uses the exact (erf) GELU.
+ *  - TTT-MLP uses the erf form of GELU, x * Phi(x) (the kernel evaluates erf
+ *    to within 1.5e-7, Abramowitz & Stegun 7.1.26).
  *
  * Conventions for every entry point:
  *  - Memory: the caller allocates every buffer (device memory unless stated)

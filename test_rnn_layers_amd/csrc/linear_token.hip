@@ -29,17 +29,23 @@ __global__ __launch_bounds__(256) void linear_token_kernel(LinearArgs a) {
 
     __shared__ float sq[2][kD], sk[2][kD], sv[2][kD];
     __shared__ float pz[2][4][kD], pzb[2][4][kD];
+    // rotary cos and signed sin at position p (mod K <= 16) for column c
+    __shared__ float rcs[16][kD], rsn[16][kD];
 
     float *Wc = a.W + (int64_t)ch * kD * kD;
     float *Gc = a.Wg + (int64_t)ch * kD * kD;
+    // a call that starts on a mini-batch boundary finds the accumulated
+    // gradients cleared (every commit clears them), so it does not read them
+    const bool g_clear = a.pos0 % a.K == 0;
     float Ws[16], Gs[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         Ws[i] = Wc[(16 * rg + i) * kD + c];
-        Gs[i] = Gc[(16 * rg + i) * kD + c];
+        Gs[i] = g_clear ? 0.f : Gc[(16 * rg + i) * kD + c];
     }
     float bs = a.b[(int64_t)ch * kD + c];
-    float gbs = a.bg[(int64_t)ch * kD + c];
+    float gbs = g_clear ? 0.f : a.bg[(int64_t)ch * kD + c];
+    bool committed = false;  // W_s, b_s change only at a commit
     const float gam = a.ln_w[hi * kD + c];
     const float bet = a.ln_b[hi * kD + c];
 
@@ -49,9 +55,16 @@ __global__ __launch_bounds__(256) void linear_token_kernel(LinearArgs a) {
     const float *ep = a.eta + bi * a.eta_sB + hi * a.eta_sH;
     Tout *op = (Tout *)a.out.p + bi * a.out.sB + hi * a.out.sH;
 
-    // rotary frequency of the pair containing column c (pairs c, c ^ 32)
-    const int ci = c & 31;
-    const double inv_freq = pow((double)a.rope_base, -2.0 * (double)ci / (double)kD);
+    if (a.rope) {
+        // angle p * base^(-2i/D) for the pair (i, i + 32) holding column c
+        for (int e = tid; e < 16 * kD; e += 256) {
+            const int p = e / kD, cc = e % kD;
+            const double th = (double)p * pow((double)a.rope_base, -2.0 * (double)(cc & 31) / (double)kD);
+            rcs[p][cc] = (float)cos(th);
+            rsn[p][cc] = (cc < 32 ? -1.f : 1.f) * (float)sin(th);  // x*cos - x_pair*sin | x*cos + x_pair*sin
+        }
+        __syncthreads();
+    }
 
     for (int t = 0; t < a.ntok; ++t) {
         const int buf = t & 1;
@@ -63,10 +76,8 @@ __global__ __launch_bounds__(256) void linear_token_kernel(LinearArgs a) {
             if (a.rope) {
                 const float qo = to_f32(qp[(int64_t)tok * a.q.sL + (c ^ 32)]);
                 const float ko = to_f32(kp[(int64_t)tok * a.k.sL + (c ^ 32)]);
-                const double th = (double)(pos % a.K) * inv_freq;
-                const float cs = (float)cos(th), sn = (float)sin(th);
-                // first half: x*cos - x_pair*sin ; second half: x*cos + x_pair*sin
-                const float sg = (c < 32) ? -sn : sn;
+                const int p = (int)(pos % a.K);
+                const float cs = rcs[p][c], sg = rsn[p][c];
                 qv = qv * cs + qo * sg;
                 kv = kv * cs + ko * sg;
             }
@@ -122,16 +133,21 @@ __global__ __launch_bounds__(256) void linear_token_kernel(LinearArgs a) {
             }
             bs -= gbs;
             gbs = 0.f;
+            committed = true;
         }
     }
+    // write back what changed: W_s, b_s after a commit; the gradients unless
+    // they were clear in memory and are clear again
+    const bool g_clear_out = (a.pos0 + a.ntok) % a.K == 0;
+    if (committed) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        Wc[(16 * rg + i) * kD + c] = Ws[i];
-        Gc[(16 * rg + i) * kD + c] = Gs[i];
+        for (int i = 0; i < 16; ++i) Wc[(16 * rg + i) * kD + c] = Ws[i];
+        if (rg == 0) a.b[(int64_t)ch * kD + c] = bs;
     }
-    if (rg == 0) {
-        a.b[(int64_t)ch * kD + c] = bs;
-        a.bg[(int64_t)ch * kD + c] = gbs;
+    if (!(g_clear && g_clear_out)) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Gc[(16 * rg + i) * kD + c] = Gs[i];
+        if (rg == 0) a.bg[(int64_t)ch * kD + c] = gbs;
     }
 }
 

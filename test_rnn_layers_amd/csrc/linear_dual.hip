@@ -641,8 +641,13 @@ __device__ void col_main(const LinearArgs &a, Smem<T> &sm, int ch, int c, int g,
     if (g == 0) a.b[(int64_t)ch * kD + 16 * c + n] = Bt[0];
 }
 
+// fp16 operands fit 128 VGPRs, so two chains share a CU when there are more
+// chains than CUs; the fp32-operand variant keeps its larger register file
+template <typename T>
+constexpr int kWavesPerSimd = std::is_same<T, _Float16>::value ? 4 : 1;
+
 template <typename Tin, typename Tout, typename T, bool ROPE>
-__global__ __launch_bounds__(512, 1) void linear_dual_kernel(LinearArgs a) {
+__global__ __launch_bounds__(512, kWavesPerSimd<T>) void linear_dual_kernel(LinearArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Smem<T> &sm = *reinterpret_cast<Smem<T> *>(smem_raw);
     const int ch = blockIdx.x;

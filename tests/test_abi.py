@@ -127,3 +127,74 @@ def test_state_init_errors():
     assert T.STATUS_NAMES[lib.ttt_linear_state_init(ctypes.byref(_cfg(D=16)), _addr(1), _addr(4), ctypes.byref(st),
                                                     None)] == "TTT_ERR_SHAPE"
     assert st.offset == 5
+
+
+# ---------------------------------------------------------------------------
+# TTT-MLP entry points
+# ---------------------------------------------------------------------------
+F = 256
+
+
+def _mlp_cfg(**kw):
+    c = T.mlp_cfg(B, H, in_dtype="bf16", out_dtype="f32")
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def _mlp_state(offset=0, **over):
+    p = [_addr(20 + i) for i in range(8)]
+    for i, v in over.items():
+        p[int(i[1:])] = v
+    return T.ttt_mlp_state(*p, offset)
+
+
+def _mlp_call(**over):
+    a = dict(cfg=_mlp_cfg(), L=L, XQ=T.ttt_tensor(_addr(0), H * L * D, L * D, D),
+             XK=T.ttt_tensor(_addr(1), H * L * D, L * D, D), XV=T.ttt_tensor(_addr(2), H * L * D, L * D, D),
+             eta=T.ttt_eta(_addr(3), 0, L), ln_w=_addr(4), ln_b=_addr(5), state=_mlp_state(),
+             out=T.ttt_tensor(_addr(10), H * L * D, L * D, D))
+    a.update(over)
+    cfg = ctypes.byref(a["cfg"]) if a["cfg"] is not None else None
+    st = ctypes.byref(a["state"]) if a["state"] is not None else None
+    rc = T.load().ttt_mlp_prefill(cfg, a["L"], a["XQ"], a["XK"], a["XV"], a["eta"], a["ln_w"], a["ln_b"], st,
+                                  a["out"], None)
+    return rc, a
+
+
+MLP_CASES = [
+    ("null cfg", dict(cfg=None), "TTT_ERR_NULL"),
+    ("null state", dict(state=None), "TTT_ERR_NULL"),
+    ("null W2_grad", dict(state=_mlp_state(s6=None)), "TTT_ERR_NULL"),
+    ("null XV", dict(XV=T.ttt_tensor(None, H * L * D, L * D, D)), "TTT_ERR_NULL"),
+    ("F=128", dict(cfg=_mlp_cfg(F=128)), "TTT_ERR_SHAPE"),
+    ("K=8", dict(cfg=_mlp_cfg(K=8)), "TTT_ERR_SHAPE"),
+    ("D=32", dict(cfg=_mlp_cfg(D=32)), "TTT_ERR_SHAPE"),
+    ("L=0", dict(L=0), "TTT_ERR_SHAPE"),
+    ("fp32 inputs", dict(cfg=_mlp_cfg(in_dtype=T.TTT_F32)), "TTT_ERR_UNSUPPORTED"),
+    ("open mini-batch offset", dict(state=_mlp_state(offset=5)), "TTT_ERR_UNSUPPORTED"),
+    ("negative offset", dict(state=_mlp_state(offset=-16)), "TTT_ERR_STATE"),
+    ("misaligned b1", dict(state=_mlp_state(s1=_addr(21) + 4)), "TTT_ERR_ALIGN"),
+    ("state buffers overlap", dict(state=_mlp_state(s3=_addr(20) + 1024)), "TTT_ERR_ALIAS"),
+    ("out overlaps XK", dict(out=T.ttt_tensor(_addr(1), H * L * D, L * D, D)), "TTT_ERR_ALIAS"),
+    ("out overlaps state", dict(out=T.ttt_tensor(_addr(24), H * L * D, L * D, D)), "TTT_ERR_ALIAS"),
+]
+
+
+@pytest.mark.parametrize("label,over,expect", MLP_CASES, ids=[c[0] for c in MLP_CASES])
+def test_mlp_error_paths(label, over, expect):
+    rc, a = _mlp_call(**over)
+    assert T.STATUS_NAMES[rc] == expect, (label, T.ttt_last_error())
+    assert T.ttt_last_error()
+    if a["state"] is not None:
+        assert a["state"].offset == over.get("state", _mlp_state()).offset  # unchanged on error
+
+
+def test_mlp_state_init_errors():
+    lib = T.load()
+    st = _mlp_state(offset=7)
+    assert T.STATUS_NAMES[lib.ttt_mlp_state_init(ctypes.byref(_mlp_cfg()), _addr(1), None, _addr(3), _addr(4),
+                                                 ctypes.byref(st), None)] == "TTT_ERR_NULL"
+    assert T.STATUS_NAMES[lib.ttt_mlp_state_init(ctypes.byref(_mlp_cfg(F=64)), _addr(1), _addr(2), _addr(3),
+                                                 _addr(4), ctypes.byref(st), None)] == "TTT_ERR_SHAPE"
+    assert st.offset == 7

@@ -39,7 +39,7 @@ constexpr int XP = 72;    // f16 row pitch of the 16x64 tiles
 constexpr int HP = 264;   // f16 row pitch of the 16x256 tiles
 constexpr int NP = 68;    // f16 row pitch of the ng2 tile
 constexpr int FP = 68;    // fp32 row pitch of the partial sums
-constexpr int kParts = 9; // 8 hidden slices + the causal term of Zb2
+constexpr int kParts = 8; // hidden slices
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -50,7 +50,6 @@ struct Smem {
     _Float16 x2[kM][HP];      // X2 = GELU(Z1), [token][hidden]
     _Float16 xb2[kM][HP];     // Xb2 = GELU(Zb1)
     _Float16 ng2[kM][NP];     // ng2, [token][d]
-    _Float16 w2h[kF][XP];     // W2 at the start of the mini-batch, [hidden][d]
     float part[kParts][kM][FP];  // partial sums of Z2 / Zb2, [slice][token][d]
     float b2[kD];             // b2 at the start of the current mini-batch
     float b2n[kD];            // b2 after its step
@@ -79,11 +78,6 @@ __device__ __forceinline__ h8 row_perm(const _Float16 *X, int pitch, int n, int 
     const h4 a = *(const h4 *)(X + n * pitch + c0 + 4 * g);
     const h4 b = *(const h4 *)(X + n * pitch + c0 + 16 + 4 * g);
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-// column c of a row-major f16 tile, tokens 4g..4g+3 (a k = 16 operand)
-__device__ __forceinline__ h4 col4(const _Float16 *X, int pitch, int c, int g) {
-    return h4{X[(4 * g) * pitch + c], X[(4 * g + 1) * pitch + c], X[(4 * g + 2) * pitch + c],
-              X[(4 * g + 3) * pitch + c]};
 }
 
 template <int CTRL>
@@ -266,6 +260,10 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
         for (int i = 0; i < 8; ++i)
             sel[h][i] = (i / 4 == h && 4 * g + (i & 3) == n) ? (_Float16)1.f : (_Float16)0.f;
     const h4 ones = h4{(_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f};
+    // the 16x16 identity as a B fragment (lane: I[4g+j][n])
+    h4 ident;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ident[j] = (4 * g + j == n) ? (_Float16)1.f : (_Float16)0.f;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     phase_barrier();
 
@@ -292,12 +290,6 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
                 sm.x2[4 * g + j][32 * w + 16 * s + n] = (_Float16)X2[s][j];
             }
         }
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sm.w2h[32 * w + 16 * s2 + 4 * g + j][16 * r + n] = (_Float16)W2s[s2][r][j];
         h4 M1;
         {
             const f32x4 st = mfma32(xp1, qp1, mfma32(xp0, qp0, zero));  // lane: S[query n][key 4g+j]
@@ -350,15 +342,22 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
         phase_barrier();  // B3: ng2 in LDS
 
         // ---- P3: ng1, Zb1, Xb2; step of W1, b1, b2 ----
-        const h8 gp0 = row_perm(&sm.ng2[0][0], NP, n, g, 0), gp1 = row_perm(&sm.ng2[0][0], NP, n, g, 32);
+        // ng2 as A fragments by column block r (lane: ng2[n][16r+4g+j]), and
+        // as B fragments (lane: ng2[4g+j][16r+n]) through an exact product
+        // with the identity
+        h4 nr[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) G2[r] = col4(&sm.ng2[0][0], NP, 16 * r + n, g);
+        for (int r = 0; r < 4; ++r) nr[r] = *(const h4 *)&sm.ng2[n][16 * r + 4 * g];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) G2[r] = to_h4(mfma16(nr[r], ident, zero));
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            // ng1 = (ng2 W2^T) o GELU'(Z1): A = ng2 rows, B = rows f of W2 (k = d)
-            const int f = 32 * w + 16 * s + n;
-            const f32x4 g1 =
-                mfma32(gp1, row_perm(&sm.w2h[0][0], XP, f, g, 32), mfma32(gp0, row_perm(&sm.w2h[0][0], XP, f, g, 0), zero));
+            // ng1 = (ng2 W2^T) o GELU'(Z1).  W2^T fragments come from this
+            // wave's W2 tiles: a tile used as the A operand against the
+            // identity gives its transpose in the B layout (exact in fp16)
+            f32x4 g1 = zero;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) g1 = mfma16(nr[r], to_h4(mfma16(to_h4(W2s[s][r]), ident, zero)), g1);
             f32x4 ng1;
 #pragma unroll
             for (int j = 0; j < 4; ++j) ng1[j] = g1[j] * D1[s][j];
@@ -385,12 +384,20 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
         }
         phase_barrier();  // B4: Xb2 in LDS
 
-        // ---- P4: partial Zb2 over this hidden slice; the causal term ----
+        // ---- P4: partial Zb2 over this hidden slice, with this slice's part
+        // of the causal term: tril(Xb2 X2^T + 1) ng2 is the sum over the
+        // slices of tril(Xb2_s X2_s^T) ng2, plus tril(1) ng2 (wave 0) ----
         {
             const h8 xb2p = row_perm(&sm.xb2[0][0], HP, n, g, 32 * w);
+            const h8 x2p = row_perm(&sm.x2[0][0], HP, n, g, 32 * w);
+            const f32x4 st = mfma32(x2p, xb2p, zero);  // lane: S[query n][key 4g+j] over the slice
+            f32x4 mm;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mm[j] = (4 * g + j <= n) ? st[j] + (w == 0 ? 1.f : 0.f) : 0.f;
+            const h4 M2 = to_h4(mm);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const f32x4 z = mfma32(xb2p, pair_b(W2s[0][r], W2s[1][r]), zero);
+                const f32x4 z = mfma16(M2, G2[r], mfma32(xb2p, pair_b(W2s[0][r], W2s[1][r]), zero));
 #pragma unroll
                 for (int j = 0; j < 4; ++j) sm.part[w][4 * g + j][16 * r + n] = z[j];
             }
@@ -401,23 +408,6 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
             for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) W2s[s][r] = mfma16(x2h[s], G2[r], W2s[s][r]);
-        }
-        if (w == 4) {
-            // M2 = tril(Xb2 X2^T + 1) over all 256 hidden units, then M2 ng2
-            f32x4 st = zero;
-#pragma unroll
-            for (int c = 0; c < kF; c += 32)
-                st = mfma32(row_perm(&sm.x2[0][0], HP, n, g, c), row_perm(&sm.xb2[0][0], HP, n, g, c), st);
-            f32x4 m;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) m[j] = (4 * g + j <= n) ? st[j] + 1.f : 0.f;
-            const h4 M2 = to_h4(m);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const f32x4 z = mfma16(M2, G2[r], zero);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sm.part[8][4 * g + j][16 * r + n] = z[j];
-            }
         }
         phase_barrier();  // B5
 

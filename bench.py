@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--rope", action="store_true", help="rotary on for a linear workload that has it off")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
+    ap.add_argument("--decode-eager", action="store_true",
+                    help="decode workload: launch the decode calls one by one instead of replaying a HIP graph")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB twice (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -357,6 +359,9 @@ def bench_mlp(args, w):
 
 
 def bench_decode(args, w):
+    """Prefill 512 tokens, then 256 single-token decode calls.  By default the
+    256 calls are captured once in a HIP graph and replayed each step (the
+    serving loop); --decode-eager launches them one by one from Python."""
     import torch
 
     from test_rnn_layers_amd import libttt
@@ -373,27 +378,50 @@ def bench_decode(args, w):
     W0, b0 = inp["W0"].to(dev).contiguous(), inp["b0"].to(dev).contiguous()
     out = torch.empty((B, H, P + T, D), dtype=odt, device=dev)
     st = libttt.LinearState.empty(B, H, D, device=dev)
-    stream = torch.cuda.current_stream()
-    tm = Timer(stream)
     # views of every decode token, made once
     views = [tuple(x[n][:, :, t:t + 1] for n in ("XQ", "XK", "XV")) + (eta[:, t:t + 1], out[:, :, t:t + 1])
              for t in range(P, P + T)]
 
-    def step(i, timed):
+    def prefill(stream):
         libttt.ttt_linear_state_init(cfg, W0, b0, st, stream)
-        if timed:
-            tm.start("prefill")
         libttt.ttt_linear_prefill(cfg, P, x["XQ"][:, :, :P], x["XK"][:, :, :P], x["XV"][:, :, :P], eta[:, :P],
                                   lw, lb, st, out[:, :, :P], stream)
+
+    def decode_all(stream, tm=None):
+        for (q, k, v, e, o) in views:
+            if tm:
+                tm.start("token")
+            libttt.ttt_linear_decode(cfg, 1, q, k, v, e, lw, lb, st, o, stream)
+            if tm:
+                tm.stop("token")
+
+    graph = None
+    if not args.decode_eager:
+        # warm up eagerly, then capture the decode calls from the post-prefill
+        # state (their positions are baked into the graph, so every replay
+        # starts from a fresh prefill)
+        prefill(torch.cuda.current_stream())
+        decode_all(torch.cuda.current_stream())
+        prefill(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            decode_all(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    tm = Timer(stream)
+
+    def step(i, timed):
+        if timed:
+            tm.start("prefill")
+        prefill(stream)
         if timed:
             tm.stop("prefill")
             tm.start("decode")
-        for j, (q, k, v, e, o) in enumerate(views):
-            if timed:
-                tm.start("token")
-            libttt.ttt_linear_decode(cfg, 1, q, k, v, e, lw, lb, st, o, stream)
-            if timed:
-                tm.stop("token")
+        if graph is not None:
+            graph.replay()
+        else:
+            decode_all(stream, tm if timed else None)
         if timed:
             tm.stop("decode")
 
@@ -403,14 +431,21 @@ def bench_decode(args, w):
     # per chain and decode call: read W_s, b_s, G, gb; write G, gb; inputs/out
     state_rw = 3 * (D * D + D) * 4
     amount = (per_tok + state_rw) * B * H
+    if graph is not None:
+        # back-to-back replayed launches: the mean launch duration is the
+        # replay time over the number of calls (gaps between launches included)
+        kms = {k: (v / T if k != "n" else v * T) for k, v in dec.items()}
+        how = "HIP graph of the 256 decode calls, replayed; per-call time = replay time / 256"
+    else:
+        kms = stats(tm.ms("token"))
+        how = "256 decode calls launched one by one from Python; per-call HIP events"
     res = common(args, w, B * T / (dec["mean"] * 1e-3), elapsed, w.dtype,
-                 {"prefill": P, "decode_steps": T, "rope": w.rope,
+                 {"prefill": P, "decode_steps": T, "rope": w.rope, "decode_launch": how,
                   "decode_phase_ms": dec, "prefill_ms": stats(tm.ms("prefill")),
-                  "value_is": "decode tokens/s over the 256 decode calls (GPU time incl. launch gaps)",
+                  "value_is": "decode tokens/s over the 256 decode calls (GPU time of the decode phase)",
                   "step_tokens_per_s": B * (P + T) * args.steps / elapsed})
     res["metric"] = f"TTT-Linear decode tokens/sec ({w.name})"
-    res["roofline"] = roofline("linear_token_kernel", w.name, bound="hbm", amount=amount,
-                               kernel_ms=stats(tm.ms("token")),
+    res["roofline"] = roofline("linear_token_kernel", w.name, bound="hbm", amount=amount, kernel_ms=kms,
                                per_unit=f"{per_tok} B token in/out + {state_rw} B state read/write per chain",
                                units=f"{B * H} chains, one token each")
     if not args.no_cpu_baseline:

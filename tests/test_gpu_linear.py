@@ -185,3 +185,46 @@ def test_many_chains_bitwise_repeatable():
         g.run(0, L)
         runs.append(g.result()[0])
     assert np.array_equal(runs[0], runs[1])
+
+
+def test_decode_graph_replays_match_eager():
+    """The decode calls captured in a HIP graph and replayed (as the
+    benchmark runs them): every replay, with eager work and synchronisation
+    in between, reproduces the eager outputs and final state bit for bit."""
+    from test_rnn_layers_amd import libttt
+
+    inp = make_inputs(2, 3, 48, dtype="bf16", seed=61, rich=True)
+    P, T = 21, 27  # the prefill ends inside a mini-batch; decode crosses two boundaries
+
+    def fresh():
+        g = LinearGPU(inp, in_dtype="bf16")
+        g.run(0, P)
+        return g
+
+    def decode_calls(g):
+        for t in range(P, P + T):
+            g.run(t, t + 1, decode=True)
+
+    ref = fresh()
+    decode_calls(ref)
+    rout, rW, rb, rG, rgb = ref.result()
+
+    g = fresh()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        decode_calls(g)
+    torch.cuda.synchronize()
+    saved = [t.clone() for t in (g.state.W, g.state.b, g.state.W_grad, g.state.b_grad)]  # post-prefill state
+    for rep in range(3):
+        # eager work between replays: restore the post-prefill state, clear the outputs
+        for dst, src in zip((g.state.W, g.state.b, g.state.W_grad, g.state.b_grad), saved):
+            dst.copy_(src)
+        g.out[:, :, P:].fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        out, W, b, G, gb = g.result()
+        assert np.array_equal(out[:, :, P:], rout[:, :, P:]), rep
+        for got, want in ((W, rW), (b, rb), (G, rG), (gb, rgb)):
+            assert np.array_equal(got, want), rep

@@ -51,6 +51,9 @@ struct Smem {
     _Float16 xb2[kM][HP];     // Xb2 = GELU(Zb1)
     _Float16 ng2[kM][NP];     // ng2, [token][d]
     float part[kParts][kM][FP];  // partial sums of Z2 / Zb2, [slice][token][d]
+    float cel[2][kM][kD];     // eta (gamma (k - v) + gamma beta), by mini-batch parity
+    float qres[2][kM][kD];    // q + beta (the residual of the output), by parity
+    float eta[2][kM];         // learning rate per token, by parity
     float b2[kD];             // b2 at the start of the current mini-batch
     float b2n[kD];            // b2 after its step
     float gam[kD], gam2[kD], bet[kD], gb[kD];  // per-column LayerNorm constants
@@ -84,12 +87,17 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
-__device__ __forceinline__ float row_sum16(float x) {
+
+// sums over the 16 lanes of the row of two values (interleaved chains)
+__device__ __forceinline__ void row_sum16x2(float &x, float &y) {
     x += dpp<0xB1>(x);
+    y += dpp<0xB1>(y);
     x += dpp<0x4E>(x);
+    y += dpp<0x4E>(y);
     x += dpp<0x141>(x);
+    y += dpp<0x141>(y);
     x += dpp<0x140>(x);
-    return x;
+    y += dpp<0x140>(y);
 }
 
 // GELU(x) = x Phi(x) and GELU'(x) = Phi(x) + x phi(x) with the erf form of
@@ -113,9 +121,20 @@ __device__ __forceinline__ float ncdf_tail(float x, float &e) {
     e = __expf(-0.5f * x * x);
     return 0.5f * poly * e;
 }
+// GELU alone needs no density, so it takes erf from formula 7.1.28 of the same
+// handbook (absolute error <= 3e-7), which has a reciprocal but no exponential:
+//   erf(z) = 1 - 1 / (1 + a1 z + ... + a6 z^6)^16,  z >= 0
+// (the 16th power overflows to +inf for large z, where 1/inf = 0 is the limit)
 __device__ __forceinline__ float gelu(float x) {
-    float e;
-    const float h = ncdf_tail(x, e);
+    constexpr float a1 = 0.0705230784f, a2 = 0.0422820123f, a3 = 0.0092705272f, a4 = 0.0001520143f,
+                    a5 = 0.0002765672f, a6 = 0.0000430638f;
+    const float z = fabsf(x) * 0.70710678118654752f;
+    float pz = fmaf(fmaf(fmaf(fmaf(fmaf(fmaf(a6, z, a5), z, a4), z, a3), z, a2), z, a1), z, 1.f);
+    pz *= pz;  // ^2
+    pz *= pz;  // ^4
+    pz *= pz;  // ^8
+    pz *= pz;  // ^16
+    const float h = 0.5f * __builtin_amdgcn_rcpf(pz);  // (1 - erf(|x| / sqrt(2))) / 2
     return x * (x >= 0.f ? 1.f - h : h);
 }
 __device__ __forceinline__ Gelu gelu_both(float x) {
@@ -141,8 +160,8 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
     const int bi = ch / a.H, hi = ch % a.H;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, n = l & 15;
     const int NB = a.nblk;  // mini-batches; the last has a.tail tokens if a.tail > 0
-    const bool lnw = w < 4; // LayerNorm / staging wave: token row 4w+g, columns 4n..4n+3
-    const int t = 4 * w + g;
+    const bool lnw = w < 4; // LayerNorm waves 0..3 and staging waves 4..7: token row 4(w%4)+g, columns 4n..4n+3
+    const int t = 4 * (w & 3) + g;
 
     // ---- state of hidden slice f in [32w, 32w+32) ----
     const int64_t cD = (int64_t)ch * kD;
@@ -218,7 +237,8 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
             x[3] = __builtin_bit_cast(float, u.w);
         }
     };
-    float cel[4], eg2[4], qres[4];
+    // staging (waves 4..7): rotated q, k as fp16 rows; the LayerNorm operands
+    // of the mini-batch into LDS for the LayerNorm waves
     auto stage = [&](const In &x, int buf) {
         float q[4], k[4], v[4];
         unpack(x.q, q);
@@ -235,23 +255,29 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
         }
         *(h4 *)&sm.qs[buf][t][4 * n] = h4{(_Float16)q[0], (_Float16)q[1], (_Float16)q[2], (_Float16)q[3]};
         *(h4 *)&sm.xs[buf][t][4 * n] = h4{(_Float16)k[0], (_Float16)k[1], (_Float16)k[2], (_Float16)k[3]};
-        const f32x4 gm = *(const f32x4 *)&sm.gam[4 * n], g2 = *(const f32x4 *)&sm.gam2[4 * n];
+        const f32x4 gm = *(const f32x4 *)&sm.gam[4 * n];
         const f32x4 bt = *(const f32x4 *)&sm.bet[4 * n], gbv = *(const f32x4 *)&sm.gb[4 * n];
+        f32x4 ce, qr;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            cel[e] = x.eta * (gm[e] * (k[e] - v[e]) + gbv[e]);
-            eg2[e] = x.eta * g2[e];
-            qres[e] = q[e] + bt[e];
+            ce[e] = x.eta * (gm[e] * (k[e] - v[e]) + gbv[e]);
+            qr[e] = q[e] + bt[e];
         }
+        *(f32x4 *)&sm.cel[buf][t][4 * n] = ce;
+        *(f32x4 *)&sm.qres[buf][t][4 * n] = qr;
+        if (n == 0) sm.eta[buf][t] = x.eta;
     };
 
     In pre;
-    if (lnw) fetch(pre, 0);
+    if (!lnw) fetch(pre, 0);
     phase_barrier();  // constants in LDS
-    if (lnw) {
+    if (!lnw) {
         stage(pre, 0);
         if (NB > 1) fetch(pre, 1);
     }
+    float gam2r[4];  // LayerNorm waves: gamma^2 at columns 4n .. 4n+3
+#pragma unroll
+    for (int e = 0; e < 4; ++e) gam2r[e] = sm.gam2[4 * n + e];
     // selection patterns for K^T fragments (see the TTT-Linear kernel)
     h8 sel[2];
 #pragma unroll
@@ -318,28 +344,38 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
             f32x4 z = *(const f32x4 *)&sm.b2[4 * n];
 #pragma unroll
             for (int p = 0; p < 8; ++p) z += *(const f32x4 *)&sm.part[p][t][4 * n];
-            const float mu = row_sum16(z[0] + z[1] + z[2] + z[3]) * (1.f / kD);
-            float d[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) d[e] = z[e] - mu;
-            const float var = row_sum16(d[0] * d[0] + d[1] * d[1] + d[2] * d[2] + d[3] * d[3]) * (1.f / kD);
-            const float rs = __builtin_amdgcn_rsqf(var + a.eps);
-            float xh[4], u[4], su = 0.f, sux = 0.f;
+            const f32x4 cel = *(const f32x4 *)&sm.cel[buf][t][4 * n];
+            const float eta = sm.eta[buf][t];
+            // mean and mean square in one reduction round
+            float s1 = (z[0] + z[1]) + (z[2] + z[3]);
+            float s2 = fmaf(z[0], z[0], z[1] * z[1]) + fmaf(z[2], z[2], z[3] * z[3]);
+            row_sum16x2(s1, s2);
+            const float mu = s1 * (1.f / kD);
+            const float var = fmaxf(fmaf(-mu, mu, s2 * (1.f / kD)), 0.f);
+            const float rs = __builtin_amdgcn_rsqf(var + a.eps);  // var + eps >= eps > 0
+            const float mrs = -mu * rs;
+            float xh[4], u[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                xh[e] = d[e] * rs;
-                u[e] = eg2[e] * xh[e] + cel[e];
-                su += u[e];
-                sux += u[e] * xh[e];
+                xh[e] = fmaf(z[e], rs, mrs);
+                u[e] = fmaf(eta * gam2r[e], xh[e], cel[e]);
             }
-            su = row_sum16(su) * (1.f / kD);
-            sux = row_sum16(sux) * (1.f / kD);
+            float su = (u[0] + u[1]) + (u[2] + u[3]);
+            float sux = fmaf(u[0], xh[0], u[1] * xh[1]) + fmaf(u[2], xh[2], u[3] * xh[3]);
+            row_sum16x2(su, sux);
+            su *= (1.f / kD);
+            sux *= (1.f / kD);
             float ng[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) ng[e] = -rs * (u[e] - su - xh[e] * sux);
             *(h4 *)&sm.ng2[t][4 * n] = h4{(_Float16)ng[0], (_Float16)ng[1], (_Float16)ng[2], (_Float16)ng[3]};
+        } else if (nb + 1 < NB) {
+            // stage the next mini-batch (its buffers were last read in P0 of nb-1
+            // and P5 of nb-1)
+            stage(pre, buf ^ 1);
+            if (nb + 2 < NB) fetch(pre, nb + 2);
         }
-        phase_barrier();  // B3: ng2 in LDS
+        phase_barrier();  // B3: ng2 in LDS, mini-batch nb+1 staged
 
         // ---- P3: ng1, Zb1, Xb2; step of W1, b1, b2 ----
         // ng2 as A fragments by column block r (lane: ng2[n][16r+4g+j]), and
@@ -416,16 +452,17 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
             f32x4 z = *(const f32x4 *)&sm.b2[4 * n];
 #pragma unroll
             for (int p = 0; p < kParts; ++p) z += *(const f32x4 *)&sm.part[p][t][4 * n];
-            const float mu = row_sum16(z[0] + z[1] + z[2] + z[3]) * (1.f / kD);
-            float d[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) d[e] = z[e] - mu;
-            const float var = row_sum16(d[0] * d[0] + d[1] * d[1] + d[2] * d[2] + d[3] * d[3]) * (1.f / kD);
-            const float rs = __builtin_amdgcn_rsqf(var + a.eps);
+            const f32x4 qres = *(const f32x4 *)&sm.qres[buf][t][4 * n];
+            float s1 = (z[0] + z[1]) + (z[2] + z[3]);
+            float s2 = fmaf(z[0], z[0], z[1] * z[1]) + fmaf(z[2], z[2], z[3] * z[3]);
+            row_sum16x2(s1, s2);
+            const float mu = s1 * (1.f / kD);
+            const float var = fmaxf(fmaf(-mu, mu, s2 * (1.f / kD)), 0.f);
+            const float rs = __builtin_amdgcn_rsqf(var + a.eps);  // var + eps >= eps > 0
             const f32x4 gm = *(const f32x4 *)&sm.gam[4 * n];
             float y[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) y[e] = d[e] * (rs * gm[e]) + qres[e];
+            for (int e = 0; e < 4; ++e) y[e] = (z[e] - mu) * (rs * gm[e]) + qres[e];
             const bool valid = !(open && t >= a.tail);
             if (valid) {
                 Tout *o = po + (int64_t)nb * kM * a.out.sL;
@@ -436,12 +473,8 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
                     *(b4 *)o = b4{(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
                 }
             }
-            if (nb + 1 < NB) {
-                stage(pre, buf ^ 1);
-                if (nb + 2 < NB) fetch(pre, nb + 2);
-            }
         }
-        phase_barrier();  // next mini-batch staged; part, x2, xb2, ng2 free
+        phase_barrier();  // part, x2, xb2, ng2 free
     }
 
     // ---- final state (an open last mini-batch left W, b at its start) ----

@@ -48,19 +48,33 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
 
-// Sum over the 64 lanes of a wavefront; every lane receives the total.
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
-    return x;
+// Sums over the 64 lanes of a wavefront; every lane receives the totals.
+// Each 16-lane row is summed with DPP lane moves (pairs, quads, half-row
+// mirror, row mirror: every lane of the row then holds the row total), and
+// the four row totals are read out through scalar registers and added in a
+// fixed order.  No LDS round trips, unlike cross-lane shuffles.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
-
-// Sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15); every lane of the
-// row receives its row's total.
-__device__ __forceinline__ float row16_sum(float x) {
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
-    return x;
+__device__ __forceinline__ float lane_value(float x, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+__device__ __forceinline__ float rows_total(float x) {
+    return ((lane_value(x, 0) + lane_value(x, 16)) + lane_value(x, 32)) + lane_value(x, 48);
+}
+// two independent sums, their DPP chains interleaved
+__device__ __forceinline__ void wave_sum2(float &x, float &y) {
+    x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+    y += dpp_mov<0xB1>(y);
+    x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+    y += dpp_mov<0x4E>(y);
+    x += dpp_mov<0x141>(x);  // row_half_mirror
+    y += dpp_mov<0x141>(y);
+    x += dpp_mov<0x140>(x);  // row_mirror
+    y += dpp_mov<0x140>(y);
+    x = rows_total(x);
+    y = rows_total(y);
 }
 
 // 16x16x32 bf16 MFMA, fp32 accumulate.

@@ -8,9 +8,14 @@
 // W - W_grad, b - b_grad; at a mini-batch boundary the step is committed and
 // the gradients cleared (TTTCache continuation, "TTTLinear.ttt").
 //
-// One workgroup of 256 threads per (batch, head) chain.  Thread t owns column
-// c = t % 64 of W and W_grad for rows 16*(t/64) .. +15, in registers for the
-// whole call, so a call over T tokens reads and writes the 33 KB state once.
+// One wave per (batch, head) chain.  Lane c owns column c of W and W_grad
+// for all 64 rows, in registers for the whole call, so a call over T tokens
+// reads and writes the 33 KB state once, and every product of a token is an
+// in-lane multiply-add chain over the token's q or k, which the lanes read
+// from LDS as broadcasts.  The only cross-lane work is the LayerNorm sums
+// (DPP within 16-lane rows, then the four row totals through scalar
+// registers); there are no barriers.  2048 chains take 2048 waves, which the
+// chip holds at once.
 // Used for decoding, for the tokens that complete an open mini-batch before a
 // prefill, for a trailing partial mini-batch, and for mini-batch sizes the
 // dual-form MFMA kernel does not take.
@@ -20,15 +25,12 @@
 namespace ttt {
 
 template <typename Tin, typename Tout>
-__global__ __launch_bounds__(256) void linear_token_kernel(LinearArgs a) {
+__global__ __launch_bounds__(64, 2) void linear_token_kernel(LinearArgs a) {
     const int ch = blockIdx.x;
     const int bi = ch / a.H, hi = ch % a.H;
-    const int tid = threadIdx.x;
-    const int c = tid & 63;
-    const int rg = tid >> 6;
+    const int c = threadIdx.x;  // column
 
-    __shared__ float sq[2][kD], sk[2][kD], sv[2][kD];
-    __shared__ float pz[2][4][kD], pzb[2][4][kD];
+    __shared__ __align__(16) float sq[kD], sk[kD];
     // rotary cos and signed sin at position p (mod K <= 16) for column c
     __shared__ float rcs[16][kD], rsn[16][kD];
 
@@ -37,11 +39,15 @@ __global__ __launch_bounds__(256) void linear_token_kernel(LinearArgs a) {
     // a call that starts on a mini-batch boundary finds the accumulated
     // gradients cleared (every commit clears them), so it does not read them
     const bool g_clear = a.pos0 % a.K == 0;
-    float Ws[16], Gs[16];
+    float Ws[kD], Gs[kD];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        Ws[i] = Wc[(16 * rg + i) * kD + c];
-        Gs[i] = g_clear ? 0.f : Gc[(16 * rg + i) * kD + c];
+    for (int i = 0; i < kD; ++i) Ws[i] = Wc[i * kD + c];
+    if (g_clear) {
+#pragma unroll
+        for (int i = 0; i < kD; ++i) Gs[i] = 0.f;
+    } else {
+#pragma unroll
+        for (int i = 0; i < kD; ++i) Gs[i] = Gc[i * kD + c];
     }
     float bs = a.b[(int64_t)ch * kD + c];
     float gbs = g_clear ? 0.f : a.bg[(int64_t)ch * kD + c];
@@ -57,77 +63,82 @@ __global__ __launch_bounds__(256) void linear_token_kernel(LinearArgs a) {
 
     if (a.rope) {
         // angle p * base^(-2i/D) for the pair (i, i + 32) holding column c
-        for (int e = tid; e < 16 * kD; e += 256) {
-            const int p = e / kD, cc = e % kD;
-            const double th = (double)p * pow((double)a.rope_base, -2.0 * (double)(cc & 31) / (double)kD);
-            rcs[p][cc] = (float)cos(th);
-            rsn[p][cc] = (cc < 32 ? -1.f : 1.f) * (float)sin(th);  // x*cos - x_pair*sin | x*cos + x_pair*sin
+        for (int p = 0; p < 16; ++p) {
+            const double th = (double)p * pow((double)a.rope_base, -2.0 * (double)(c & 31) / (double)kD);
+            rcs[p][c] = (float)cos(th);
+            rsn[p][c] = (c < 32 ? -1.f : 1.f) * (float)sin(th);  // x*cos - x_pair*sin | x*cos + x_pair*sin
         }
-        __syncthreads();
     }
 
     for (int t = 0; t < a.ntok; ++t) {
-        const int buf = t & 1;
         const int tok = a.t0 + t;
         const int64_t pos = a.pos0 + t;
-        if (rg == 0) {
-            float qv = to_f32(qp[(int64_t)tok * a.q.sL + c]);
-            float kv = to_f32(kp[(int64_t)tok * a.k.sL + c]);
-            if (a.rope) {
-                const float qo = to_f32(qp[(int64_t)tok * a.q.sL + (c ^ 32)]);
-                const float ko = to_f32(kp[(int64_t)tok * a.k.sL + (c ^ 32)]);
-                const int p = (int)(pos % a.K);
-                const float cs = rcs[p][c], sg = rsn[p][c];
-                qv = qv * cs + qo * sg;
-                kv = kv * cs + ko * sg;
-            }
-            sq[buf][c] = qv;
-            sk[buf][c] = kv;
-            sv[buf][c] = to_f32(vp[(int64_t)tok * a.v.sL + c]);
-        }
+        float qv = to_f32(qp[(int64_t)tok * a.q.sL + c]);
+        float kv = to_f32(kp[(int64_t)tok * a.k.sL + c]);
+        const float vv = to_f32(vp[(int64_t)tok * a.v.sL + c]);
         const float e = ep[tok];
-        __syncthreads();
+        if (a.rope) {
+            const float qo = to_f32(qp[(int64_t)tok * a.q.sL + (c ^ 32)]);
+            const float ko = to_f32(kp[(int64_t)tok * a.k.sL + (c ^ 32)]);
+            const int p = (int)(pos % a.K);
+            const float cs = rcs[p][c], sg = rsn[p][c];
+            qv = qv * cs + qo * sg;
+            kv = kv * cs + ko * sg;
+        }
+        // one wave: its LDS accesses execute in order, so the reads below see
+        // these writes (and the next token's writes follow these reads)
+        sq[c] = qv;
+        sk[c] = kv;
 
-        // Z1 = k W + b at the mini-batch-start state
-        float zp = 0.f;
+        // z = k W + b at the mini-batch-start state (four interleaved chains)
+        float z4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) zp += sk[buf][16 * rg + i] * Ws[i];
-        pz[buf][rg][c] = zp;
-        __syncthreads();
-        const float z = pz[buf][0][c] + pz[buf][1][c] + pz[buf][2][c] + pz[buf][3][c] + bs;
+        for (int i = 0; i < kD; i += 4) {
+            const f32x4 k4 = *(const f32x4 *)&sk[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) z4[j] = fmaf(k4[j], Ws[i + j], z4[j]);
+        }
+        const float z = ((z4[0] + z4[1]) + (z4[2] + z4[3])) + bs;
 
-        // gradient of 1/2 ||LN(z) - (v - k)||^2 (every wave holds the whole row)
-        const float mu = wave_sum(z) * (1.f / kD);
-        const float d = z - mu;
-        const float rs = rsqrtf(wave_sum(d * d) * (1.f / kD) + a.eps);
-        const float xh = d * rs;
-        const float u = gam * (gam * xh + bet - (sv[buf][c] - sk[buf][c]));
-        const float su = wave_sum(u) * (1.f / kD);
-        const float sux = wave_sum(u * xh) * (1.f / kD);
+        // gradient of 1/2 ||LN(z) - (v - k)||^2; mean and mean square in one
+        // reduction, as do mean(u) and mean(u xhat)
+        float s1 = z, s2 = z * z;
+        wave_sum2(s1, s2);
+        const float mu = s1 * (1.f / kD);
+        const float var = fmaxf(fmaf(-mu, mu, s2 * (1.f / kD)), 0.f);
+        const float rs = rsqrtf(var + a.eps);
+        const float xh = (z - mu) * rs;
+        const float u = gam * (gam * xh + bet - (vv - kv));
+        float su = u, sux = u * xh;
+        wave_sum2(su, sux);
+        su *= (1.f / kD);
+        sux *= (1.f / kD);
         const float g = (u - su - xh * sux) * rs;
 
         // accumulate the eta-weighted gradient; prediction with W - W_grad
         const float eg = e * g;
-        float zbp = 0.f;
+        float zb4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float kr = sk[buf][16 * rg + i];
-            Gs[i] += kr * eg;
-            zbp += sq[buf][16 * rg + i] * (Ws[i] - Gs[i]);
+        for (int i = 0; i < kD; i += 4) {
+            const f32x4 k4 = *(const f32x4 *)&sk[i];
+            const f32x4 q4 = *(const f32x4 *)&sq[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                Gs[i + j] = fmaf(k4[j], eg, Gs[i + j]);
+                zb4[j] = fmaf(q4[j], Ws[i + j] - Gs[i + j], zb4[j]);
+            }
         }
         gbs += eg;
-        pzb[buf][rg][c] = zbp;
-        __syncthreads();
-        const float zb = pzb[buf][0][c] + pzb[buf][1][c] + pzb[buf][2][c] + pzb[buf][3][c] + bs - gbs;
-        if (rg == 0) {
-            const float mu2 = wave_sum(zb) * (1.f / kD);
-            const float d2 = zb - mu2;
-            const float rs2 = rsqrtf(wave_sum(d2 * d2) * (1.f / kD) + a.eps);
-            op[(int64_t)tok * a.out.sL + c] = from_f32<Tout>(sq[buf][c] + gam * d2 * rs2 + bet);
-        }
+        const float zb = ((zb4[0] + zb4[1]) + (zb4[2] + zb4[3])) + (bs - gbs);
+        float t1 = zb, t2 = zb * zb;
+        wave_sum2(t1, t2);
+        const float mu2 = t1 * (1.f / kD);
+        const float rs2 = rsqrtf(fmaxf(fmaf(-mu2, mu2, t2 * (1.f / kD)), 0.f) + a.eps);
+        op[(int64_t)tok * a.out.sL + c] = from_f32<Tout>(qv + gam * (zb - mu2) * rs2 + bet);
+
         if ((pos + 1) % a.K == 0) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 0; i < kD; ++i) {
                 Ws[i] -= Gs[i];
                 Gs[i] = 0.f;
             }
@@ -141,13 +152,13 @@ __global__ __launch_bounds__(256) void linear_token_kernel(LinearArgs a) {
     const bool g_clear_out = (a.pos0 + a.ntok) % a.K == 0;
     if (committed) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) Wc[(16 * rg + i) * kD + c] = Ws[i];
-        if (rg == 0) a.b[(int64_t)ch * kD + c] = bs;
+        for (int i = 0; i < kD; ++i) Wc[i * kD + c] = Ws[i];
+        a.b[(int64_t)ch * kD + c] = bs;
     }
     if (!(g_clear && g_clear_out)) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) Gc[(16 * rg + i) * kD + c] = Gs[i];
-        if (rg == 0) a.bg[(int64_t)ch * kD + c] = gbs;
+        for (int i = 0; i < kD; ++i) Gc[i * kD + c] = Gs[i];
+        a.bg[(int64_t)ch * kD + c] = gbs;
     }
 }
 
@@ -159,7 +170,7 @@ __global__ void tile_kernel(float *dst, const float *src, int64_t per, int64_t t
 }
 
 hipError_t launch_linear_token(const LinearArgs &a, int in_bf16, int out_bf16, hipStream_t s) {
-    dim3 grid(a.B * a.H), block(256);
+    dim3 grid(a.B * a.H), block(kWave);
     if (in_bf16 && out_bf16)
         hipLaunchKernelGGL((linear_token_kernel<__bf16, __bf16>), grid, block, 0, s, a);
     else if (in_bf16)

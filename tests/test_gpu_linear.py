@@ -83,6 +83,19 @@ def test_decode_steps_f32():
     _check_full("decode_f32", inp, dtype="f32", pieces=cuts, decode=set(cuts))
 
 
+def test_decode_steps_rope_bf16():
+    """Single-token decode calls with rotary at position mod K, bf16 inputs."""
+    inp = make_inputs(2, 3, 50, dtype="bf16", seed=41, rich=True)
+    cuts = [18] + list(range(19, 50))
+    _check_full("decode_rope_bf16", inp, dtype="bf16", rope=True, pieces=cuts, decode=set(cuts))
+
+
+def test_other_minibatch_size_rope():
+    """K = 13: every token on the token kernel, rotary at position mod 13."""
+    inp = make_inputs(1, 2, 45, dtype="bf16", seed=57, rich=True)
+    _check_full("K13_rope", inp, dtype="bf16", K=13, rope=True, pieces=[9])
+
+
 def test_bf16_output():
     inp = make_inputs(2, 2, 64, dtype="bf16", seed=8)
     _check_full("bf16_out", inp, dtype="bf16", out_dtype="bf16")

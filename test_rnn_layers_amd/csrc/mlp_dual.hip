@@ -40,6 +40,7 @@ constexpr int HP = 264;   // f16 row pitch of the 16x256 tiles
 constexpr int NP = 68;    // f16 row pitch of the ng2 tile
 constexpr int FP = 68;    // fp32 row pitch of the partial sums
 constexpr int kParts = 8; // hidden slices
+constexpr int TP = 20;    // f16 pitch of the transposed 64x16 tiles (rows 40 B apart)
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -47,6 +48,8 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 struct Smem {
     _Float16 xs[2][kM][XP];   // K rows (rotated), double-buffered by mini-batch
     _Float16 qs[2][kM][XP];   // Q rows (rotated)
+    _Float16 kT[2][kD][TP];   // K^T (rotated), [d][token], by parity
+    _Float16 ng2T[kD][TP];    // ng2^T, [d][token]
     _Float16 x2[kM][HP];      // X2 = GELU(Z1), [token][hidden]
     _Float16 xb2[kM][HP];     // Xb2 = GELU(Zb1)
     _Float16 ng2[kM][NP];     // ng2, [token][d]
@@ -253,8 +256,11 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
                 k[e] = k[e] * c4[e] + ko * s4[e];
             }
         }
+        const h4 kh = h4{(_Float16)k[0], (_Float16)k[1], (_Float16)k[2], (_Float16)k[3]};
         *(h4 *)&sm.qs[buf][t][4 * n] = h4{(_Float16)q[0], (_Float16)q[1], (_Float16)q[2], (_Float16)q[3]};
-        *(h4 *)&sm.xs[buf][t][4 * n] = h4{(_Float16)k[0], (_Float16)k[1], (_Float16)k[2], (_Float16)k[3]};
+        *(h4 *)&sm.xs[buf][t][4 * n] = kh;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.kT[buf][4 * n + e][t] = kh[e];
         const f32x4 gm = *(const f32x4 *)&sm.gam[4 * n];
         const f32x4 bt = *(const f32x4 *)&sm.bet[4 * n], gbv = *(const f32x4 *)&sm.gb[4 * n];
         f32x4 ce, qr;
@@ -278,13 +284,6 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
     float gam2r[4];  // LayerNorm waves: gamma^2 at columns 4n .. 4n+3
 #pragma unroll
     for (int e = 0; e < 4; ++e) gam2r[e] = sm.gam2[4 * n + e];
-    // selection patterns for K^T fragments (see the TTT-Linear kernel)
-    h8 sel[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            sel[h][i] = (i / 4 == h && 4 * g + (i & 3) == n) ? (_Float16)1.f : (_Float16)0.f;
     const h4 ones = h4{(_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f};
     // the 16x16 identity as a B fragment (lane: I[4g+j][n])
     h4 ident;
@@ -293,8 +292,9 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     phase_barrier();
 
-    // operands of the last step, kept for an open last mini-batch
-    h4 kt[4], n1k[2], x2h[2], G2[4];
+    // operands of the last step, kept for an open last mini-batch (the K^T
+    // and ng2 fragments are re-read from LDS, which keeps the last block's)
+    h4 n1k[2], x2h[2];
     for (int nb = 0; nb < NB; ++nb) {
         const int buf = nb & 1;
         const bool open = (nb == NB - 1) && a.tail > 0;  // partial last mini-batch: keep W, emit grads
@@ -324,8 +324,6 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
             for (int j = 0; j < 4; ++j) m[j] = (4 * g + j <= n) ? st[j] + 1.f : 0.f;
             M1 = to_h4(m);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) kt[r] = to_h4(mfma32(r < 2 ? xp0 : xp1, sel[r & 1], zero));
         if (nb > 0 && threadIdx.x < kD) sm.b2[threadIdx.x] = sm.b2n[threadIdx.x];  // previous step
         phase_barrier();  // B1: X2 in LDS, b2 current
 
@@ -365,10 +363,12 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
             row_sum16x2(su, sux);
             su *= (1.f / kD);
             sux *= (1.f / kD);
-            float ng[4];
+            h4 ngh;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ng[e] = -rs * (u[e] - su - xh[e] * sux);
-            *(h4 *)&sm.ng2[t][4 * n] = h4{(_Float16)ng[0], (_Float16)ng[1], (_Float16)ng[2], (_Float16)ng[3]};
+            for (int e = 0; e < 4; ++e) ngh[e] = (_Float16)(-rs * (u[e] - su - xh[e] * sux));
+            *(h4 *)&sm.ng2[t][4 * n] = ngh;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.ng2T[4 * n + e][t] = ngh[e];
         } else if (nb + 1 < NB) {
             // stage the next mini-batch (its buffers were last read in P0 of nb-1
             // and P5 of nb-1)
@@ -379,13 +379,13 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
 
         // ---- P3: ng1, Zb1, Xb2; step of W1, b1, b2 ----
         // ng2 as A fragments by column block r (lane: ng2[n][16r+4g+j]), and
-        // as B fragments (lane: ng2[4g+j][16r+n]) through an exact product
-        // with the identity
-        h4 nr[4];
+        // as B fragments (lane: ng2[4g+j][16r+n]) from the transposed copy
+        h4 nr[4], G2[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) nr[r] = *(const h4 *)&sm.ng2[n][16 * r + 4 * g];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) G2[r] = to_h4(mfma16(nr[r], ident, zero));
+        for (int r = 0; r < 4; ++r) {
+            nr[r] = *(const h4 *)&sm.ng2[n][16 * r + 4 * g];
+            G2[r] = *(const h4 *)&sm.ng2T[16 * r + n][4 * g];
+        }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             // ng1 = (ng2 W2^T) o GELU'(Z1).  W2^T fragments come from this
@@ -404,8 +404,11 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
             x2h[s] = to_h4(X2[s]);
             n1k[s] = n1;
             if (!open) {
+                // W1 += X^T ng1, with K^T rows 16r .. 16r+15 as A fragments
+                // (lane: K[4g+j][16r+n], from the transposed copy)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) W1s[s][r] = mfma16(kt[r], n1, W1s[s][r]);  // W1 += X^T ng1
+                for (int r = 0; r < 4; ++r)
+                    W1s[s][r] = mfma16(*(const h4 *)&sm.kT[buf][16 * r + n][4 * g], n1, W1s[s][r]);
                 b1t[s] = mfma16(ones, n1, b1t[s]);
             }
         }
@@ -486,9 +489,12 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
             const int f0 = 32 * w + 16 * s;
             float *g1p = a.W1g + cD * kF + (4 * g) * kF + f0 + n;
             float *g2p = a.W2g + cD * kF + (f0 + 4 * g) * kD + n;
+            const int lb = (NB - 1) & 1;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const f32x4 d1 = mfma16(kt[r], n1k[s], zero), d2 = mfma16(x2h[s], G2[r], zero);
+                const h4 kt = *(const h4 *)&sm.kT[lb][16 * r + n][4 * g];
+                const h4 g2 = *(const h4 *)&sm.ng2T[16 * r + n][4 * g];
+                const f32x4 d1 = mfma16(kt, n1k[s], zero), d2 = mfma16(x2h[s], g2, zero);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     g1p[(16 * r + j) * kF] = -d1[j];

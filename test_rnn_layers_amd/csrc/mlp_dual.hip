@@ -18,12 +18,16 @@
 //  * wave w owns hidden units f in [32w, 32w+32): its 64x32 slab of W1 and
 //    its 32x64 slab of W2, as fp32 MFMA accumulator tiles for the whole
 //    chain; the backward product ng2 W2^T contracts over the other index of
-//    W2, so each mini-batch also leaves an fp16 row copy of W2 in LDS;
+//    W2, whose fragments come from this wave's tiles by identity products;
 //  * Z1, Zb1, ng1, X2 stay in registers in accumulator layout, which is also
 //    the operand layout of the M1 ng1 correction and of the three state
 //    updates; X2, Xb2 and ng2 go through LDS where a row layout is needed;
 //  * Z2 and Zb2 are sums over the 8 hidden slices: partial tiles in LDS,
-//    summed by the LayerNorm waves 0..3 (16 lanes per token row, DPP sums);
+//    summed by the LayerNorm waves 0..3 (16 lanes per token row, DPP sums),
+//    which also leave a transposed fp16 copy of ng2 (its B fragments);
+//  * waves 4..7 stage the next mini-batch while waves 0..3 run the LayerNorm
+//    backward: rotated q, k as fp16 rows and a transposed copy of k (the K^T
+//    fragments of the W1 step), and the LayerNorm operands in fp32;
 //  * operands are fp16 (bf16 inputs), accumulation fp32; GELU in the erf form.
 #include <type_traits>
 

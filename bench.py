@@ -41,6 +41,28 @@ def linear_token_bytes(in_dtype, out_dtype):
     return 3 * D * e[in_dtype] + 4 + D * e[out_dtype]
 
 
+def decode_state_bytes(layout, positions):
+    """Mean state bytes one chain reads and writes per decode call, over the
+    calls at `positions`.  Every call reads W_s, b_s; a call that closes the
+    mini-batch writes them.  Dense layout: read W_grad, b_grad unless the
+    mini-batch is empty, write them.  Rows layout: read the p open rows
+    [k_j | eta_j g_j] and b_grad, write the row added (none when the call
+    closes the mini-batch) and b_grad."""
+    wb = (D * D + D) * 4
+    total = 0
+    for pos in positions:
+        p = pos % K
+        n = wb
+        if layout == "dense":
+            n += (wb if p else 0) + wb
+        else:
+            n += p * 2 * D * 4 + (D * 4 if p else 0) + (2 * D * 4 if p != K - 1 else 0) + D * 4
+        if p == K - 1:
+            n += wb
+        total += n
+    return total / len(positions)
+
+
 # the state a prefill chain reads once and writes once: W, b (fp32)
 LINEAR_STATE_BYTES = 2 * (D * D + D) * 4
 # the state of one TTT-MLP chain, read once and written once: W1, b1, W2, b2
@@ -64,6 +86,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
     ap.add_argument("--decode-eager", action="store_true",
                     help="decode workload: launch the decode calls one by one instead of replaying a HIP graph")
+    ap.add_argument("--grad-layout", default="rows", choices=["rows", "dense"],
+                    help="decode workload: how the state holds the open mini-batch's gradient (the rows "
+                         "[k_j | eta_j g_j], or their dense sum W_grad)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB twice (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -370,7 +395,8 @@ def bench_decode(args, w):
     dev = "cuda"
     B, H, P, T = w.B, w.H, w.prefill, w.decode
     inp = workload_inputs(w)
-    cfg = libttt.linear_cfg(B, H, in_dtype=w.dtype, out_dtype=args.out_dtype, rope=w.rope)
+    cfg = libttt.linear_cfg(B, H, in_dtype=w.dtype, out_dtype=args.out_dtype, rope=w.rope,
+                            grad_layout=args.grad_layout)
     odt = torch.float32 if args.out_dtype == "f32" else torch.bfloat16
     x = {n: inp[n].to(dev).contiguous() for n in ("XQ", "XK", "XV")}
     eta = inp["eta"].to(dev).contiguous()
@@ -428,8 +454,9 @@ def bench_decode(args, w):
     elapsed = run_steps(args, step)
     dec = stats(tm.ms("decode"))
     per_tok = linear_token_bytes(w.dtype, args.out_dtype)
-    # per chain and decode call: read W_s, b_s, G, gb; write G, gb; inputs/out
-    state_rw = 3 * (D * D + D) * 4
+    # per chain and decode call: the state read and written (mean over the
+    # 256 positions), the token's inputs and output
+    state_rw = decode_state_bytes(args.grad_layout, range(P, P + T))
     amount = (per_tok + state_rw) * B * H
     if graph is not None:
         # back-to-back replayed launches: the mean launch duration is the
@@ -441,12 +468,14 @@ def bench_decode(args, w):
         how = "256 decode calls launched one by one from Python; per-call HIP events"
     res = common(args, w, B * T / (dec["mean"] * 1e-3), elapsed, w.dtype,
                  {"prefill": P, "decode_steps": T, "rope": w.rope, "decode_launch": how,
+                  "grad_layout": args.grad_layout,
                   "decode_phase_ms": dec, "prefill_ms": stats(tm.ms("prefill")),
                   "value_is": "decode tokens/s over the 256 decode calls (GPU time of the decode phase)",
                   "step_tokens_per_s": B * (P + T) * args.steps / elapsed})
     res["metric"] = f"TTT-Linear decode tokens/sec ({w.name})"
     res["roofline"] = roofline("linear_token_kernel", w.name, bound="hbm", amount=amount, kernel_ms=kms,
-                               per_unit=f"{per_tok} B token in/out + {state_rw} B state read/write per chain",
+                               per_unit=f"{per_tok} B token in/out + {state_rw:g} B state read/write per chain "
+                                        f"({args.grad_layout} W_grad, mean over the decode positions)",
                                units=f"{B * H} chains, one token each")
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_decode(inp, w, args.cpu_seconds)

@@ -110,15 +110,37 @@ typedef struct ttt_linear_cfg {
     int32_t rope;        /* 1: rotary embedding at position mod K on q and k */
     float rope_base;     /* rotary base, e.g. 10000 */
     float ln_eps;        /* LayerNorm eps, e.g. 1e-6 */
+    int32_t grad_layout; /* ttt_grad_layout of state->W_grad (0: dense) */
 } ttt_linear_cfg;
+
+/* How state->W_grad holds the open mini-batch's gradient sum
+ * G = sum_j eta_j k_j^T g_j (j = 0 .. offset % K - 1, k_j after rotary):
+ *   TTT_GRAD_DENSE : G itself, [D, D] per chain (the pages' cache key).
+ *   TTT_GRAD_ROWS  : the rows that make it up.  Per chain the [D, D] buffer is
+ *                    read as [D/2, 2D]: row j = [k_j (D values), eta_j g_j
+ *                    (D values)] for j < offset % K; rows past that are
+ *                    undefined.  A call reads offset % K rows and writes the
+ *                    ones it adds, instead of reading and writing all of G:
+ *                    ~22 KB instead of ~50 KB of state traffic per chain and
+ *                    decoded token.  Outputs, W, b and b_grad are the same
+ *                    function of the inputs in both layouts (up to rounding
+ *                    order); G is the sum of the rows' outer products.
+ * The layout is a property of the state: use one layout for all calls on a
+ * state (state_init writes zeros, valid in both). */
+typedef enum ttt_grad_layout {
+    TTT_GRAD_DENSE = 0,
+    TTT_GRAD_ROWS = 1
+} ttt_grad_layout;
 
 /* TTTCache-style carried state of TTT-Linear (all fp32, device, contiguous):
  *   W      [B, H, D, D]  mini-batch-start weights, row r = input dim
  *   b      [B, H, D]     mini-batch-start bias
- *   W_grad [B, H, D, D]  sum over the open mini-batch of eta_j k_j^T g_j
+ *   W_grad [B, H, D, D]  the open mini-batch's sum of eta_j k_j^T g_j, in
+ *                        cfg->grad_layout
  *   b_grad [B, H, D]     sum over the open mini-batch of eta_j g_j
  *   offset (host)        tokens consumed so far (the cache's seqlen_offset);
- *                        W_grad and b_grad are zero whenever offset % K == 0. */
+ *                        W_grad and b_grad are zero whenever offset % K == 0
+ *                        (in the rows layout no row is open then). */
 typedef struct ttt_linear_state {
     float *W, *b, *W_grad, *b_grad;
     int64_t offset;

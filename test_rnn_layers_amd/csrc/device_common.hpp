@@ -39,6 +39,7 @@ struct LinearArgs {
     int32_t rope;
     float rope_base;
     float eps;
+    int32_t grad_rows;          // W_grad holds the open mini-batch's rows [k_j | eta_j g_j]
 };
 
 __device__ __forceinline__ float to_f32(float x) { return x; }

@@ -24,7 +24,14 @@
 
 namespace ttt {
 
-template <typename Tin, typename Tout>
+constexpr int kRP = 68;  // f32 pitch of the open rows of k (rows 4 banks apart)
+
+// ROWS: W_grad holds the open mini-batch's rows [k_j | eta_j g_j] instead of
+// their sum G.  Then q (W_s - G) = q W_s - sum_j (q . k_j) eta_j g_j: lane j
+// forms q . k_j for the open rows j, and the sum runs over those scalars; the
+// state read per call is W_s and the open rows, and a call writes only the
+// rows it adds (and W_s, b_s at a commit).
+template <typename Tin, typename Tout, bool ROWS>
 __global__ __launch_bounds__(64, 2) void linear_token_kernel(LinearArgs a) {
     const int ch = blockIdx.x;
     const int bi = ch / a.H, hi = ch % a.H;
@@ -33,16 +40,26 @@ __global__ __launch_bounds__(64, 2) void linear_token_kernel(LinearArgs a) {
     __shared__ __align__(16) float sq[kD], sk[kD];
     // rotary cos and signed sin at position p (mod K <= 16) for column c
     __shared__ float rcs[16][kD], rsn[16][kD];
+    // ROWS: k_j and eta_j g_j of the open rows j < 16 of the current mini-batch
+    __shared__ __align__(16) float kr[ROWS ? 16 : 1][ROWS ? kRP : 4];
+    __shared__ float er[ROWS ? 16 : 1][kD];
 
     float *Wc = a.W + (int64_t)ch * kD * kD;
     float *Gc = a.Wg + (int64_t)ch * kD * kD;
+    const int K = a.K;
+    const int p0 = (int)(a.pos0 % K);  // rows of the open mini-batch at the start
     // a call that starts on a mini-batch boundary finds the accumulated
     // gradients cleared (every commit clears them), so it does not read them
-    const bool g_clear = a.pos0 % a.K == 0;
-    float Ws[kD], Gs[kD];
+    const bool g_clear = p0 == 0;
+    float Ws[kD], Gs[ROWS ? 1 : kD];
 #pragma unroll
     for (int i = 0; i < kD; ++i) Ws[i] = Wc[i * kD + c];
-    if (g_clear) {
+    if constexpr (ROWS) {
+        for (int j = 0; j < p0; ++j) {
+            kr[j][c] = Gc[j * 2 * kD + c];
+            er[j][c] = Gc[j * 2 * kD + kD + c];
+        }
+    } else if (g_clear) {
 #pragma unroll
         for (int i = 0; i < kD; ++i) Gs[i] = 0.f;
     } else {
@@ -73,6 +90,7 @@ __global__ __launch_bounds__(64, 2) void linear_token_kernel(LinearArgs a) {
     for (int t = 0; t < a.ntok; ++t) {
         const int tok = a.t0 + t;
         const int64_t pos = a.pos0 + t;
+        const int p = (int)(pos % K);  // row of this token in its mini-batch
         float qv = to_f32(qp[(int64_t)tok * a.q.sL + c]);
         float kv = to_f32(kp[(int64_t)tok * a.k.sL + c]);
         const float vv = to_f32(vp[(int64_t)tok * a.v.sL + c]);
@@ -80,7 +98,6 @@ __global__ __launch_bounds__(64, 2) void linear_token_kernel(LinearArgs a) {
         if (a.rope) {
             const float qo = to_f32(qp[(int64_t)tok * a.q.sL + (c ^ 32)]);
             const float ko = to_f32(kp[(int64_t)tok * a.k.sL + (c ^ 32)]);
-            const int p = (int)(pos % a.K);
             const float cs = rcs[p][c], sg = rsn[p][c];
             qv = qv * cs + qo * sg;
             kv = kv * cs + ko * sg;
@@ -117,30 +134,77 @@ __global__ __launch_bounds__(64, 2) void linear_token_kernel(LinearArgs a) {
 
         // accumulate the eta-weighted gradient; prediction with W - W_grad
         const float eg = e * g;
-        float zb4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < kD; i += 4) {
-            const f32x4 k4 = *(const f32x4 *)&sk[i];
-            const f32x4 q4 = *(const f32x4 *)&sq[i];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                Gs[i + j] = fmaf(k4[j], eg, Gs[i + j]);
-                zb4[j] = fmaf(q4[j], Ws[i + j] - Gs[i + j], zb4[j]);
-            }
-        }
         gbs += eg;
-        const float zb = ((zb4[0] + zb4[1]) + (zb4[2] + zb4[3])) + (bs - gbs);
+        float zb;
+        if constexpr (ROWS) {
+            kr[p][c] = kv;
+            er[p][c] = eg;
+            // lane j <= p: q . k_j over the open rows, this token's included
+            float sj = 0.f;
+            if (c <= p) {
+                float d4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < kD; i += 4) {
+                    const f32x4 q4 = *(const f32x4 *)&sq[i];
+                    const f32x4 k4 = *(const f32x4 *)&kr[c][i];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) d4[j] = fmaf(q4[j], k4[j], d4[j]);
+                }
+                sj = (d4[0] + d4[1]) + (d4[2] + d4[3]);
+            }
+            float zq4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < kD; i += 4) {
+                const f32x4 q4 = *(const f32x4 *)&sq[i];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) zq4[j] = fmaf(q4[j], Ws[i + j], zq4[j]);
+            }
+            float qg = 0.f;  // (q G)[c] = sum_j (q . k_j) eta_j g_j[c]
+            for (int j = 0; j <= p; ++j) qg = fmaf(lane_value(sj, j), er[j][c], qg);
+            zb = (((zq4[0] + zq4[1]) + (zq4[2] + zq4[3])) - qg) + (bs - gbs);
+        } else {
+            float zb4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < kD; i += 4) {
+                const f32x4 k4 = *(const f32x4 *)&sk[i];
+                const f32x4 q4 = *(const f32x4 *)&sq[i];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    Gs[i + j] = fmaf(k4[j], eg, Gs[i + j]);
+                    zb4[j] = fmaf(q4[j], Ws[i + j] - Gs[i + j], zb4[j]);
+                }
+            }
+            zb = ((zb4[0] + zb4[1]) + (zb4[2] + zb4[3])) + (bs - gbs);
+        }
         float t1 = zb, t2 = zb * zb;
         wave_sum2(t1, t2);
         const float mu2 = t1 * (1.f / kD);
         const float rs2 = rsqrtf(fmaxf(fmaf(-mu2, mu2, t2 * (1.f / kD)), 0.f) + a.eps);
         op[(int64_t)tok * a.out.sL + c] = from_f32<Tout>(qv + gam * (zb - mu2) * rs2 + bet);
 
-        if ((pos + 1) % a.K == 0) {
+        if (p == K - 1) {
+            if constexpr (ROWS) {
+                // W_s -= sum_j k_j^T (eta_j g_j), summed over j in token order
+                float acc[kD];
 #pragma unroll
-            for (int i = 0; i < kD; ++i) {
-                Ws[i] -= Gs[i];
-                Gs[i] = 0.f;
+                for (int i = 0; i < kD; ++i) acc[i] = 0.f;
+                for (int j = 0; j < K; ++j) {
+                    const float ej = er[j][c];
+#pragma unroll
+                    for (int i = 0; i < kD; i += 4) {
+                        const f32x4 k4 = *(const f32x4 *)&kr[j][i];
+#pragma unroll
+                        for (int l = 0; l < 4; ++l) acc[i + l] = fmaf(k4[l], ej, acc[i + l]);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < kD; ++i) Ws[i] -= acc[i];
+            } else {
+#pragma unroll
+                for (int i = 0; i < kD; ++i) {
+                    Ws[i] -= Gs[i];
+                    Gs[i] = 0.f;
+                }
             }
             bs -= gbs;
             gbs = 0.f;
@@ -149,17 +213,24 @@ __global__ __launch_bounds__(64, 2) void linear_token_kernel(LinearArgs a) {
     }
     // write back what changed: W_s, b_s after a commit; the gradients unless
     // they were clear in memory and are clear again
-    const bool g_clear_out = (a.pos0 + a.ntok) % a.K == 0;
+    const int p_end = (int)((a.pos0 + a.ntok) % K);
+    const bool g_clear_out = p_end == 0;
     if (committed) {
 #pragma unroll
         for (int i = 0; i < kD; ++i) Wc[i * kD + c] = Ws[i];
         a.b[(int64_t)ch * kD + c] = bs;
     }
-    if (!(g_clear && g_clear_out)) {
+    if constexpr (ROWS) {
+        // the rows this call added to the mini-batch left open
+        for (int j = committed ? 0 : p0; j < p_end; ++j) {
+            Gc[j * 2 * kD + c] = kr[j][c];
+            Gc[j * 2 * kD + kD + c] = er[j][c];
+        }
+    } else if (!(g_clear && g_clear_out)) {
 #pragma unroll
         for (int i = 0; i < kD; ++i) Gc[i * kD + c] = Gs[i];
-        a.bg[(int64_t)ch * kD + c] = gbs;
     }
+    if (!(g_clear && g_clear_out)) a.bg[(int64_t)ch * kD + c] = gbs;
 }
 
 // dst[b, i] = src[i % per] for b < copies: tiles a per-head parameter over the
@@ -169,16 +240,24 @@ __global__ void tile_kernel(float *dst, const float *src, int64_t per, int64_t t
     if (i < total) dst[i] = src ? src[i % per] : 0.f;
 }
 
-hipError_t launch_linear_token(const LinearArgs &a, int in_bf16, int out_bf16, hipStream_t s) {
+template <bool ROWS>
+void launch_token_layout(const LinearArgs &a, int in_bf16, int out_bf16, hipStream_t s) {
     dim3 grid(a.B * a.H), block(kWave);
     if (in_bf16 && out_bf16)
-        hipLaunchKernelGGL((linear_token_kernel<__bf16, __bf16>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((linear_token_kernel<__bf16, __bf16, ROWS>), grid, block, 0, s, a);
     else if (in_bf16)
-        hipLaunchKernelGGL((linear_token_kernel<__bf16, float>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((linear_token_kernel<__bf16, float, ROWS>), grid, block, 0, s, a);
     else if (out_bf16)
-        hipLaunchKernelGGL((linear_token_kernel<float, __bf16>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((linear_token_kernel<float, __bf16, ROWS>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((linear_token_kernel<float, float>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((linear_token_kernel<float, float, ROWS>), grid, block, 0, s, a);
+}
+
+hipError_t launch_linear_token(const LinearArgs &a, int in_bf16, int out_bf16, hipStream_t s) {
+    if (a.grad_rows)
+        launch_token_layout<true>(a, in_bf16, out_bf16, s);
+    else
+        launch_token_layout<false>(a, in_bf16, out_bf16, s);
     return hipGetLastError();
 }
 

@@ -204,6 +204,7 @@ LinearArgs linear_args(const ttt_linear_cfg *cfg, const Act &x, ttt_linear_state
     a.rope = cfg->rope;
     a.rope_base = cfg->rope_base;
     a.eps = cfg->ln_eps;
+    a.grad_rows = cfg->grad_layout == TTT_GRAD_ROWS;
     return a;
 }
 
@@ -221,6 +222,8 @@ ttt_status linear_call(Mode mode, const ttt_linear_cfg *cfg, int32_t L, const Ac
                           cfg->rope_base, cfg->rope)))
         return s;
     if (L < 1) return fail(TTT_ERR_SHAPE, "token count %d must be >= 1", L);
+    if (cfg->grad_layout != TTT_GRAD_DENSE && cfg->grad_layout != TTT_GRAD_ROWS)
+        return fail(TTT_ERR_UNSUPPORTED, "unknown grad_layout %d", (int)cfg->grad_layout);
     std::vector<Range> sr;
     if ((s = check_linear_state(cfg, st, sr))) return s;
     if ((s = check_acts(x, cfg->B, cfg->H, L, cfg->D, cfg->in_dtype, cfg->out_dtype, sr))) return s;

@@ -17,6 +17,7 @@ TTT_OK = 0
 STATUS_NAMES = {0: "TTT_OK", 1: "TTT_ERR_NULL", 2: "TTT_ERR_SHAPE", 3: "TTT_ERR_DTYPE", 4: "TTT_ERR_ALIGN",
                 5: "TTT_ERR_ALIAS", 6: "TTT_ERR_STATE", 7: "TTT_ERR_UNSUPPORTED", 8: "TTT_ERR_HIP"}
 TTT_F32, TTT_BF16 = 0, 1
+TTT_GRAD_DENSE, TTT_GRAD_ROWS = 0, 1
 
 EXPORTS = ["ttt_linear_state_init", "ttt_linear_prefill", "ttt_linear_decode", "ttt_mlp_state_init",
            "ttt_mlp_prefill", "ttt_status_string", "ttt_last_error"]
@@ -32,7 +33,8 @@ class ttt_eta(ctypes.Structure):
 
 class ttt_linear_cfg(ctypes.Structure):
     _fields_ = [("B", c_int32), ("H", c_int32), ("D", c_int32), ("K", c_int32), ("in_dtype", c_int32),
-                ("out_dtype", c_int32), ("rope", c_int32), ("rope_base", c_float), ("ln_eps", c_float)]
+                ("out_dtype", c_int32), ("rope", c_int32), ("rope_base", c_float), ("ln_eps", c_float),
+                ("grad_layout", c_int32)]
 
 
 class ttt_linear_state(ctypes.Structure):
@@ -187,8 +189,11 @@ class MlpState:
         return self.struct.offset
 
 
-def linear_cfg(B, H, *, K=16, in_dtype="bf16", out_dtype="f32", rope=False, rope_base=10000.0, ln_eps=1e-6, D=64):
-    return ttt_linear_cfg(B, H, D, K, dtype_code(in_dtype), dtype_code(out_dtype), int(rope), rope_base, ln_eps)
+def linear_cfg(B, H, *, K=16, in_dtype="bf16", out_dtype="f32", rope=False, rope_base=10000.0, ln_eps=1e-6, D=64,
+               grad_layout="dense"):
+    layout = {"dense": TTT_GRAD_DENSE, "rows": TTT_GRAD_ROWS}.get(grad_layout, grad_layout)
+    return ttt_linear_cfg(B, H, D, K, dtype_code(in_dtype), dtype_code(out_dtype), int(rope), rope_base, ln_eps,
+                          int(layout))
 
 
 def mlp_cfg(B, H, *, F=256, K=16, in_dtype="bf16", out_dtype="f32", rope=False, rope_base=10000.0, ln_eps=1e-6,

@@ -25,11 +25,13 @@ class LinearGPU:
     """One TTT-Linear problem on the GPU: device inputs, state, out."""
 
     def __init__(self, inp: dict, *, K=16, rope=False, in_dtype="bf16", out_dtype="f32", layout="bhld",
-                 device="cuda"):
+                 device="cuda", grad_layout="dense"):
         self.inp = inp
         B, H, L, D = inp["XQ"].shape
         self.B, self.H, self.L, self.D = B, H, L, D
-        self.cfg = libttt.linear_cfg(B, H, K=K, in_dtype=in_dtype, out_dtype=out_dtype, rope=rope)
+        self.grad_layout = grad_layout
+        self.cfg = libttt.linear_cfg(B, H, K=K, in_dtype=in_dtype, out_dtype=out_dtype, rope=rope,
+                                     grad_layout=grad_layout)
         self.K, self.rope, self.out_dtype = K, rope, out_dtype
         self.layout = layout
         self.x = {n: self._place(inp[n].to(device)) for n in ("XQ", "XK", "XV")}
@@ -57,9 +59,16 @@ class LinearGPU:
            self.eta[:, sl], self.ln_w, self.ln_b, self.state, self.out[:, :, sl])
 
     def result(self):
+        """out, W, b, and the dense W_grad (built from the open rows in the rows
+        layout: sum_j k_j (x) eta_j g_j), b_grad."""
         torch.cuda.synchronize()
         s = self.state
-        return (to_f64(self.out), to_f64(s.W), to_f64(s.b), to_f64(s.W_grad), to_f64(s.b_grad))
+        G = to_f64(s.W_grad)
+        if self.grad_layout == "rows":
+            B, H, D = self.B, self.H, self.D
+            rows = G.reshape(B, H, D // 2, 2 * D)[:, :, : s.offset % self.cfg.K]
+            G = np.einsum("bhji,bhjc->bhic", rows[..., :D], rows[..., D:])
+        return (to_f64(self.out), to_f64(s.W), to_f64(s.b), G, to_f64(s.b_grad))
 
 
 def oracle_linear(inp: dict, *, K=16, rope=False, chains=None, L=None):

@@ -16,11 +16,12 @@ def _report(name, **kv):
           flush=True)
 
 
-def _check_full(name, inp, *, dtype, rope=False, K=16, pieces=None, layout="bhld", out_dtype="f32", decode=()):
+def _check_full(name, inp, *, dtype, rope=False, K=16, pieces=None, layout="bhld", out_dtype="f32", decode=(),
+                grad_layout="dense"):
     """Run the GPU on [0, L) split at `pieces` (list of cut points), compare
     every output and the final state with the oracle."""
     B, H, L, D = inp["XQ"].shape
-    g = LinearGPU(inp, K=K, rope=rope, in_dtype=dtype, out_dtype=out_dtype, layout=layout)
+    g = LinearGPU(inp, K=K, rope=rope, in_dtype=dtype, out_dtype=out_dtype, layout=layout, grad_layout=grad_layout)
     cuts = [0] + list(pieces or []) + [L]
     for i in range(len(cuts) - 1):
         g.run(cuts[i], cuts[i + 1], decode=cuts[i] in decode)
@@ -94,6 +95,27 @@ def test_other_minibatch_size_rope():
     """K = 13: every token on the token kernel, rotary at position mod 13."""
     inp = make_inputs(1, 2, 45, dtype="bf16", seed=57, rich=True)
     _check_full("K13_rope", inp, dtype="bf16", K=13, rope=True, pieces=[9])
+
+
+# the rows layout of W_grad (the open mini-batch's k_j and eta_j g_j rows
+# instead of their sum): same outputs and state, compared with the oracle
+@pytest.mark.parametrize("cuts", [[5], [3, 40, 41, 57], [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15]])
+def test_rows_layout_pieces(cuts):
+    inp = make_inputs(2, 2, 70, dtype="f32", seed=23, rich=True)
+    _check_full(f"rows_pieces_{cuts}", inp, dtype="f32", pieces=cuts, grad_layout="rows")
+
+
+def test_rows_layout_decode_rope_bf16():
+    inp = make_inputs(2, 3, 50, dtype="bf16", seed=41, rich=True)
+    cuts = [18] + list(range(19, 50))
+    _check_full("rows_decode_rope_bf16", inp, dtype="bf16", rope=True, pieces=cuts, decode=set(cuts),
+                grad_layout="rows")
+
+
+@pytest.mark.parametrize("K", [1, 13])
+def test_rows_layout_other_minibatch_sizes(K):
+    inp = make_inputs(1, 3, 40, dtype="f32", seed=31 + K, rich=True)
+    _check_full(f"rows_K{K}", inp, dtype="f32", K=K, pieces=[7, 20], grad_layout="rows")
 
 
 def test_bf16_output():
@@ -182,6 +204,33 @@ def test_decode_workload():
     assert max(errs) <= tol_for("bf16")
     assert max_abs(out, out2) <= tol_for("bf16")
     assert max_abs(W, W2) <= 1e-3 * max(1.0, np.abs(W2).max())
+
+
+def test_decode_workload_rows_layout():
+    """The decode workload with the rows layout: the same outputs and W, b as
+    the dense layout (to rounding), and the oracle on sampled chains."""
+    w = WORKLOADS[4]
+    inp = workload_inputs(w)
+    B, H, L, D = inp["XQ"].shape
+    res = {}
+    for layout in ("dense", "rows"):
+        g = LinearGPU(inp, in_dtype="bf16", grad_layout=layout)
+        g.run(0, w.prefill)
+        for t in range(w.prefill, L - 5):
+            g.run(t, t + 1, decode=True)
+        res[layout] = g.result()
+        assert g.state.offset == L - 5
+    chains = [(0, 0), (33, 9), (63, 31)]
+    ro, rW, rb, rG, rgb = oracle_linear(inp, chains=chains, L=L - 5)
+    out, W, b, G, gb = res["rows"]
+    errs = [max_abs(out[bb, h, : L - 5], ro[i]) for i, (bb, h) in enumerate(chains)]
+    gerr = max(max_abs(G[bb, h], rG[i]) for i, (bb, h) in enumerate(chains))
+    _report(w.name + "_rows", err=max(errs), G=gerr, rows_vs_dense=max_abs(out[:, :, : L - 5], res["dense"][0][:, :, : L - 5]))
+    assert max(errs) <= tol_for("bf16")
+    assert gerr <= tol_for("bf16") * max(1.0, float(np.abs(rG).max()))
+    assert max_abs(out[:, :, : L - 5], res["dense"][0][:, :, : L - 5]) <= tol_for("bf16")
+    assert max_abs(W, res["dense"][1]) <= 1e-3 * max(1.0, np.abs(W).max())
+    assert max_abs(G, res["dense"][3]) <= 1e-3 * max(1.0, np.abs(G).max())
 
 
 def test_many_chains_bitwise_repeatable():

@@ -51,13 +51,58 @@ __global__ __launch_bounds__(64, 2) void linear_token_kernel(LinearArgs a) {
     // a call that starts on a mini-batch boundary finds the accumulated
     // gradients cleared (every commit clears them), so it does not read them
     const bool g_clear = p0 == 0;
+
+    const Tin *qp = (const Tin *)a.q.p + bi * a.q.sB + hi * a.q.sH;
+    const Tin *kp = (const Tin *)a.k.p + bi * a.k.sB + hi * a.k.sH;
+    const Tin *vp = (const Tin *)a.v.p + bi * a.v.sB + hi * a.v.sH;
+    const float *ep = a.eta + bi * a.eta_sB + hi * a.eta_sH;
+    Tout *op = (Tout *)a.out.p + bi * a.out.sB + hi * a.out.sH;
+    // a token's inputs for column c (and the rotary partner column c ^ 32)
+    struct TokIn {
+        Tin q, k, v, qo, ko;
+        float e;
+    };
+    auto load_tok = [&](int tok) {
+        TokIn r;
+        r.q = qp[(int64_t)tok * a.q.sL + c];
+        r.k = kp[(int64_t)tok * a.k.sL + c];
+        r.v = vp[(int64_t)tok * a.v.sL + c];
+        r.e = ep[tok];
+        if (a.rope) {
+            r.qo = qp[(int64_t)tok * a.q.sL + (c ^ 32)];
+            r.ko = kp[(int64_t)tok * a.k.sL + (c ^ 32)];
+        }
+        return r;
+    };
+    // every load of the state and of the first token is issued before the
+    // first wait, so a call pays one memory round trip before its compute;
+    // the open rows go first, so the work that needs only them can start
+    // while W_s is still arriving
+    float kk[ROWS ? 16 : 1], ee[ROWS ? 16 : 1];
+    if constexpr (ROWS) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (j < p0) {
+                kk[j] = Gc[j * 2 * kD + c];
+                ee[j] = Gc[j * 2 * kD + kD + c];
+            }
+        }
+    }
+    TokIn nxt = load_tok(a.t0);
+    float bs = a.b[(int64_t)ch * kD + c];
+    float gbs = g_clear ? 0.f : a.bg[(int64_t)ch * kD + c];
+    const float gam = a.ln_w[hi * kD + c];
+    const float bet = a.ln_b[hi * kD + c];
     float Ws[kD], Gs[ROWS ? 1 : kD];
 #pragma unroll
     for (int i = 0; i < kD; ++i) Ws[i] = Wc[i * kD + c];
     if constexpr (ROWS) {
-        for (int j = 0; j < p0; ++j) {
-            kr[j][c] = Gc[j * 2 * kD + c];
-            er[j][c] = Gc[j * 2 * kD + kD + c];
+        // rows past the open ones hold zeros, so the sum over the 16 rows in
+        // the prediction needs no bound
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            kr[j][c] = j < p0 ? kk[j] : 0.f;
+            er[j][c] = j < p0 ? ee[j] : 0.f;
         }
     } else if (g_clear) {
 #pragma unroll
@@ -66,21 +111,14 @@ __global__ __launch_bounds__(64, 2) void linear_token_kernel(LinearArgs a) {
 #pragma unroll
         for (int i = 0; i < kD; ++i) Gs[i] = Gc[i * kD + c];
     }
-    float bs = a.b[(int64_t)ch * kD + c];
-    float gbs = g_clear ? 0.f : a.bg[(int64_t)ch * kD + c];
     bool committed = false;  // W_s, b_s change only at a commit
-    const float gam = a.ln_w[hi * kD + c];
-    const float bet = a.ln_b[hi * kD + c];
-
-    const Tin *qp = (const Tin *)a.q.p + bi * a.q.sB + hi * a.q.sH;
-    const Tin *kp = (const Tin *)a.k.p + bi * a.k.sB + hi * a.k.sH;
-    const Tin *vp = (const Tin *)a.v.p + bi * a.v.sB + hi * a.v.sH;
-    const float *ep = a.eta + bi * a.eta_sB + hi * a.eta_sH;
-    Tout *op = (Tout *)a.out.p + bi * a.out.sB + hi * a.out.sH;
 
     if (a.rope) {
-        // angle p * base^(-2i/D) for the pair (i, i + 32) holding column c
-        for (int p = 0; p < 16; ++p) {
+        // angle p * base^(-2i/D) for the pair (i, i + 32) holding column c, at
+        // the positions p (mod K) this call's tokens take
+        const int np = a.ntok < K ? a.ntok : K;
+        for (int n = 0; n < np; ++n) {
+            const int p = (p0 + n) % K;
             const double th = (double)p * pow((double)a.rope_base, -2.0 * (double)(c & 31) / (double)kD);
             rcs[p][c] = (float)cos(th);
             rsn[p][c] = (c < 32 ? -1.f : 1.f) * (float)sin(th);  // x*cos - x_pair*sin | x*cos + x_pair*sin
@@ -91,16 +129,18 @@ __global__ __launch_bounds__(64, 2) void linear_token_kernel(LinearArgs a) {
         const int tok = a.t0 + t;
         const int64_t pos = a.pos0 + t;
         const int p = (int)(pos % K);  // row of this token in its mini-batch
-        float qv = to_f32(qp[(int64_t)tok * a.q.sL + c]);
-        float kv = to_f32(kp[(int64_t)tok * a.k.sL + c]);
-        const float vv = to_f32(vp[(int64_t)tok * a.v.sL + c]);
-        const float e = ep[tok];
+        const TokIn in = nxt;
+        // the next token's inputs load during this token (the last token
+        // reloads its own: no branch in the loop)
+        nxt = load_tok(t + 1 < a.ntok ? tok + 1 : tok);
+        float qv = to_f32(in.q);
+        float kv = to_f32(in.k);
+        const float vv = to_f32(in.v);
+        const float e = in.e;
         if (a.rope) {
-            const float qo = to_f32(qp[(int64_t)tok * a.q.sL + (c ^ 32)]);
-            const float ko = to_f32(kp[(int64_t)tok * a.k.sL + (c ^ 32)]);
             const float cs = rcs[p][c], sg = rsn[p][c];
-            qv = qv * cs + qo * sg;
-            kv = kv * cs + ko * sg;
+            qv = qv * cs + to_f32(in.qo) * sg;
+            kv = kv * cs + to_f32(in.ko) * sg;
         }
         // one wave: its LDS accesses execute in order, so the reads below see
         // these writes (and the next token's writes follow these reads)
@@ -159,8 +199,12 @@ __global__ __launch_bounds__(64, 2) void linear_token_kernel(LinearArgs a) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) zq4[j] = fmaf(q4[j], Ws[i + j], zq4[j]);
             }
-            float qg = 0.f;  // (q G)[c] = sum_j (q . k_j) eta_j g_j[c]
-            for (int j = 0; j <= p; ++j) qg = fmaf(lane_value(sj, j), er[j][c], qg);
+            // (q G)[c] = sum_j (q . k_j) eta_j g_j[c]; rows j > p add zero
+            // (sj is zero on lanes past p, and those rows are finite)
+            float qg4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < 16; ++j) qg4[j & 3] = fmaf(lane_value(sj, j), er[j][c], qg4[j & 3]);
+            const float qg = (qg4[0] + qg4[1]) + (qg4[2] + qg4[3]);
             zb = (((zq4[0] + zq4[1]) + (zq4[2] + zq4[3])) - qg) + (bs - gbs);
         } else {
             float zb4[4] = {0.f, 0.f, 0.f, 0.f};

@@ -52,16 +52,16 @@ def load():
     lib.oracle_gelu.restype = _f64
     lib.oracle_gelu_grad.argtypes = [_f64]
     lib.oracle_gelu_grad.restype = _f64
-    chain_common = [_dp, _dp, _dp, _i64, _dp, _i64, _dp, _dp, _i32, _f64, _f64]
+    chain_common = [_dp, _dp, _dp, _i64, _dp, _i64, _dp, _dp, _dp, _i32, _f64, _f64]
     lib.oracle_linear_chain.argtypes = [_i32, _i32, _i32, _i64] + chain_common + [_dp, _dp, _dp, _dp, _dp, _i64]
     lib.oracle_linear_chain_dual.argtypes = [_i32, _i32, _i32, _i64] + chain_common + [_dp, _dp, _dp, _i64]
     lib.oracle_linear_chain_dual.restype = _i32
     lib.oracle_mlp_chain.argtypes = [_i32, _i32, _i32, _i32, _i64] + chain_common + [_dp] * 9 + [_i64]
     lib.oracle_mlp_chain_dual.argtypes = [_i32, _i32, _i32, _i32, _i64] + chain_common + [_dp] * 5 + [_i64]
     lib.oracle_mlp_chain_dual.restype = _i32
-    lib.oracle_linear_batch.argtypes = ([_i32] * 5 + [_i64, _dp, _dp, _dp, _dp, _i64, _dp, _dp, _i32, _f64, _f64]
-                                        + [_dp] * 5)
-    lib.oracle_mlp_batch.argtypes = ([_i32] * 6 + [_i64, _dp, _dp, _dp, _dp, _i64, _dp, _dp, _i32, _f64, _f64]
+    lib.oracle_linear_batch.argtypes = ([_i32] * 5 + [_i64, _dp, _dp, _dp, _dp, _i64, _dp, _dp, _dp, _i32, _f64,
+                                                       _f64] + [_dp] * 5)
+    lib.oracle_mlp_batch.argtypes = ([_i32] * 6 + [_i64, _dp, _dp, _dp, _dp, _i64, _dp, _dp, _dp, _i32, _f64, _f64]
                                      + [_dp] * 9)
     lib.oracle_max_threads.restype = _i32
     _lib = lib
@@ -75,6 +75,16 @@ def _p(a: np.ndarray):
 
 def _f(a) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _te(token_eta, K):
+    """token_eta: None (all ones) or K values, the scale of output row i of a
+    mini-batch (and, for i = K - 1, of the committed step)."""
+    if token_eta is None:
+        return None, None
+    te = _f(token_eta)
+    assert te.shape == (K,), f"token_eta must hold K = {K} values"
+    return te, _p(te)
 
 
 def ln_fwd(z, gamma, beta, eps=1e-6):
@@ -107,23 +117,25 @@ def gelu_grad(x: float) -> float:
 
 
 def linear_chain(q, k, v, eta, gamma, beta, W, b, G, gb, *, K, offset=0, rope=False,
-                 rope_base=10000.0, eps=1e-6):
-    """One chain, primal form.  q, k, v: [L, D]; eta: [L].  W, b, G, gb are
-    float64 arrays updated in place.  Returns out [L, D]."""
+                 rope_base=10000.0, eps=1e-6, token_eta=None):
+    """One chain, primal form.  q, k, v: [L, D]; eta: [L]; token_eta: [K] or
+    None.  W, b, G, gb are float64 arrays updated in place.  Returns out [L, D]."""
     q, k, v, eta, gamma, beta = map(_f, (q, k, v, eta, gamma, beta))
+    te, tp = _te(token_eta, K)
     L, D = q.shape
     out = np.empty((L, D))
-    load().oracle_linear_chain(D, K, L, offset, _p(q), _p(k), _p(v), D, _p(eta), 1, _p(gamma), _p(beta),
+    load().oracle_linear_chain(D, K, L, offset, _p(q), _p(k), _p(v), D, _p(eta), 1, tp, _p(gamma), _p(beta),
                                int(rope), rope_base, eps, _p(W), _p(b), _p(G), _p(gb), _p(out), D)
     return out
 
 
 def linear_chain_dual(q, k, v, eta, gamma, beta, W, b, *, K, offset=0, rope=False,
-                      rope_base=10000.0, eps=1e-6):
+                      rope_base=10000.0, eps=1e-6, token_eta=None):
     q, k, v, eta, gamma, beta = map(_f, (q, k, v, eta, gamma, beta))
+    te, tp = _te(token_eta, K)
     L, D = q.shape
     out = np.empty((L, D))
-    rc = load().oracle_linear_chain_dual(D, K, L, offset, _p(q), _p(k), _p(v), D, _p(eta), 1, _p(gamma),
+    rc = load().oracle_linear_chain_dual(D, K, L, offset, _p(q), _p(k), _p(v), D, _p(eta), 1, tp, _p(gamma),
                                          _p(beta), int(rope), rope_base, eps, _p(W), _p(b), _p(out), D)
     if rc != 0:
         raise ValueError("dual form needs whole aligned mini-batches")
@@ -131,24 +143,26 @@ def linear_chain_dual(q, k, v, eta, gamma, beta, W, b, *, K, offset=0, rope=Fals
 
 
 def mlp_chain(q, k, v, eta, gamma, beta, W1, b1, W2, b2, G1, gb1, G2, gb2, *, K, offset=0,
-              rope=False, rope_base=10000.0, eps=1e-6):
+              rope=False, rope_base=10000.0, eps=1e-6, token_eta=None):
     q, k, v, eta, gamma, beta = map(_f, (q, k, v, eta, gamma, beta))
+    te, tp = _te(token_eta, K)
     L, D = q.shape
     F = W1.shape[1]
     out = np.empty((L, D))
-    load().oracle_mlp_chain(D, F, K, L, offset, _p(q), _p(k), _p(v), D, _p(eta), 1, _p(gamma), _p(beta),
+    load().oracle_mlp_chain(D, F, K, L, offset, _p(q), _p(k), _p(v), D, _p(eta), 1, tp, _p(gamma), _p(beta),
                             int(rope), rope_base, eps, _p(W1), _p(b1), _p(W2), _p(b2), _p(G1), _p(gb1),
                             _p(G2), _p(gb2), _p(out), D)
     return out
 
 
 def mlp_chain_dual(q, k, v, eta, gamma, beta, W1, b1, W2, b2, *, K, offset=0, rope=False,
-                   rope_base=10000.0, eps=1e-6):
+                   rope_base=10000.0, eps=1e-6, token_eta=None):
     q, k, v, eta, gamma, beta = map(_f, (q, k, v, eta, gamma, beta))
+    te, tp = _te(token_eta, K)
     L, D = q.shape
     F = W1.shape[1]
     out = np.empty((L, D))
-    rc = load().oracle_mlp_chain_dual(D, F, K, L, offset, _p(q), _p(k), _p(v), D, _p(eta), 1, _p(gamma),
+    rc = load().oracle_mlp_chain_dual(D, F, K, L, offset, _p(q), _p(k), _p(v), D, _p(eta), 1, tp, _p(gamma),
                                       _p(beta), int(rope), rope_base, eps, _p(W1), _p(b1), _p(W2), _p(b2),
                                       _p(out), D)
     if rc != 0:
@@ -157,24 +171,26 @@ def mlp_chain_dual(q, k, v, eta, gamma, beta, W1, b1, W2, b2, *, K, offset=0, ro
 
 
 def linear_batch(XQ, XK, XV, eta, eta_sB, ln_w, ln_b, W, b, G, gb, *, K, offset=0, rope=False,
-                 rope_base=10000.0, eps=1e-6):
+                 rope_base=10000.0, eps=1e-6, token_eta=None):
     """[B, H, L, D] inputs; eta flat with batch stride eta_sB and head stride L.
     State arrays [B, H, ...] float64, updated in place.  Returns out."""
     XQ, XK, XV, eta, ln_w, ln_b = map(_f, (XQ, XK, XV, eta, ln_w, ln_b))
+    te, tp = _te(token_eta, K)
     B, H, L, D = XQ.shape
     out = np.empty_like(XQ)
-    load().oracle_linear_batch(B, H, D, K, L, offset, _p(XQ), _p(XK), _p(XV), _p(eta), eta_sB, _p(ln_w),
+    load().oracle_linear_batch(B, H, D, K, L, offset, _p(XQ), _p(XK), _p(XV), _p(eta), eta_sB, tp, _p(ln_w),
                                _p(ln_b), int(rope), rope_base, eps, _p(W), _p(b), _p(G), _p(gb), _p(out))
     return out
 
 
 def mlp_batch(XQ, XK, XV, eta, eta_sB, ln_w, ln_b, W1, b1, W2, b2, G1, gb1, G2, gb2, *, K, offset=0,
-              rope=False, rope_base=10000.0, eps=1e-6):
+              rope=False, rope_base=10000.0, eps=1e-6, token_eta=None):
     XQ, XK, XV, eta, ln_w, ln_b = map(_f, (XQ, XK, XV, eta, ln_w, ln_b))
+    te, tp = _te(token_eta, K)
     B, H, L, D = XQ.shape
     F = W1.shape[-1]
     out = np.empty_like(XQ)
-    load().oracle_mlp_batch(B, H, D, F, K, L, offset, _p(XQ), _p(XK), _p(XV), _p(eta), eta_sB, _p(ln_w),
+    load().oracle_mlp_batch(B, H, D, F, K, L, offset, _p(XQ), _p(XK), _p(XV), _p(eta), eta_sB, tp, _p(ln_w),
                             _p(ln_b), int(rope), rope_base, eps, _p(W1), _p(b1), _p(W2), _p(b2), _p(G1),
                             _p(gb1), _p(G2), _p(gb2), _p(out))
     return out

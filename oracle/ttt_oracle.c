@@ -37,8 +37,11 @@
  *   - loss is 1/2 ||r||^2 (no factor 2 in the gradient);
  *   - LayerNorm uses the population variance and eps inside the square root,
  *     for both the forward and the fused backward (bodies not on the pages);
- *   - eta_ij = token_eta_i * lr_j with token_eta == 1, so eta is one learning
- *     rate per key token; the diagonal of the causal mask is included;
+ *   - eta_ij = token_eta_i * lr_j: lr_j is the learning rate of key token j
+ *     ("ttt_lr_eta"), token_eta_i the scale of output row i within its
+ *     mini-batch ("token_eta"; te == NULL means all ones); the step committed
+ *     at a boundary uses the last row, token_eta_{K-1}; the diagonal of the
+ *     causal mask is included;
  *   - rotary embedding is rotate-half (pairs i, i + D/2), angle
  *     p * base^(-2i/D) with p = absolute position mod K, applied to q and k
  *     before everything else (target and residual use the rotated values);
@@ -149,7 +152,8 @@ static void maybe_rope(const double *x, int D, int rope, int64_t pos, int K,
 /* [P3 compute_mini_batch, primal branch; P3 TTTLinear.ttt; P2 TTTCache]   */
 /*                                                                        */
 /* q, k, v, out: L rows of D, row stride ld (elements).                   */
-/* eta: L values with stride eta_st.                                      */
+/* eta: L values with stride eta_st (the learning rate of each token).   */
+/* te: K values, token_eta by position in the mini-batch (NULL = ones).   */
 /* W: D x D row-major, W[r*D + c] maps input dim r to output dim c        */
 /*    (row vector times W, as in "X1 @ W1_init").                         */
 /* b: D.  G, gb: accumulated eta-weighted gradients of the open           */
@@ -159,9 +163,10 @@ static void maybe_rope(const double *x, int D, int rope, int64_t pos, int K,
 void oracle_linear_chain(int D, int K, int L, int64_t offset,
                          const double *q, const double *k, const double *v,
                          int64_t ld, const double *eta, int64_t eta_st,
-                         const double *gamma, const double *beta, int rope,
-                         double rope_base, double eps, double *W, double *b,
-                         double *G, double *gb, double *out, int64_t ld_out)
+                         const double *te, const double *gamma,
+                         const double *beta, int rope, double rope_base,
+                         double eps, double *W, double *b, double *G,
+                         double *gb, double *out, int64_t ld_out)
 {
     double *qr = malloc(sizeof(double) * D), *kr = malloc(sizeof(double) * D);
     double *z = malloc(sizeof(double) * D), *tgt = malloc(sizeof(double) * D);
@@ -187,20 +192,22 @@ void oracle_linear_chain(int D, int K, int L, int64_t offset,
         for (int r = 0; r < D; ++r)
             for (int c = 0; c < D; ++c) G[r * D + c] += e * kr[r] * g[c];
         for (int c = 0; c < D; ++c) gb[c] += e * g[c];
-        /* W1_bar = W1_init - grad_W1 ; Z1_bar = XQ @ W1_bar + b1_bar */
+        /* W1_bar = W1_init - token_eta * grad_W1 ; Z1_bar = XQ @ W1_bar + b1_bar */
+        double tp = te ? te[pos % K] : 1.0;
         for (int c = 0; c < D; ++c) {
-            double acc = b[c] - gb[c];
-            for (int r = 0; r < D; ++r) acc += qr[r] * (W[r * D + c] - G[r * D + c]);
+            double acc = b[c] - tp * gb[c];
+            for (int r = 0; r < D; ++r) acc += qr[r] * (W[r * D + c] - tp * G[r * D + c]);
             zb[c] = acc;
         }
         /* XQW = XQ + ln_fwd(Z1_bar) */
         oracle_ln_fwd(zb, gamma, beta, D, eps, y);
         double *ot = out + (int64_t)t * ld_out;
         for (int c = 0; c < D; ++c) ot[c] = qr[c] + y[c];
-        /* mini-batch boundary: commit the step, clear the gradients */
+        /* mini-batch boundary: commit the step of the last row (W1_last =
+         * W1_bar of token K-1), clear the gradients */
         if ((pos + 1) % K == 0) {
-            for (int i = 0; i < D * D; ++i) { W[i] -= G[i]; G[i] = 0.0; }
-            for (int c = 0; c < D; ++c) { b[c] -= gb[c]; gb[c] = 0.0; }
+            for (int i = 0; i < D * D; ++i) { W[i] -= tp * G[i]; G[i] = 0.0; }
+            for (int c = 0; c < D; ++c) { b[c] -= tp * gb[c]; gb[c] = 0.0; }
         }
     }
     free(qr); free(kr); free(z); free(tgt); free(g); free(zb); free(y);
@@ -215,9 +222,10 @@ void oracle_linear_chain(int D, int K, int L, int64_t offset,
 int oracle_linear_chain_dual(int D, int K, int L, int64_t offset,
                              const double *q, const double *k, const double *v,
                              int64_t ld, const double *eta, int64_t eta_st,
-                             const double *gamma, const double *beta, int rope,
-                             double rope_base, double eps, double *W,
-                             double *b, double *out, int64_t ld_out)
+                             const double *te, const double *gamma,
+                             const double *beta, int rope, double rope_base,
+                             double eps, double *W, double *b, double *out,
+                             int64_t ld_out)
 {
     if (offset % K != 0 || L % K != 0) return -1;
     size_t KD = (size_t)K * D;
@@ -225,14 +233,17 @@ int oracle_linear_chain_dual(int D, int K, int L, int64_t offset,
     double *Z1 = malloc(sizeof(double) * KD), *tgt = malloc(sizeof(double) * D);
     double *gZ = malloc(sizeof(double) * KD), *Zb = malloc(sizeof(double) * KD);
     double *Attn = malloc(sizeof(double) * K * K), *y = malloc(sizeof(double) * D);
-    double *et = malloc(sizeof(double) * K);
+    double *E = malloc(sizeof(double) * K * K);
     for (int n = 0; n < L / K; ++n) {
         for (int i = 0; i < K; ++i) {
             int t = n * K + i;
             maybe_rope(q + (int64_t)t * ld, D, rope, offset + t, K, rope_base, XQ + (size_t)i * D);
             maybe_rope(k + (int64_t)t * ld, D, rope, offset + t, K, rope_base, X1 + (size_t)i * D);
-            et[i] = eta[(int64_t)t * eta_st];
         }
+        /* the [K, K] eta of the block: E_ij = token_eta_i * lr_j */
+        for (int i = 0; i < K; ++i)
+            for (int j = 0; j < K; ++j)
+                E[i * K + j] = (te ? te[i] : 1.0) * eta[(int64_t)(n * K + j) * eta_st];
         /* Z1 = X1 @ W1_init + b1_init ; target = XV - XK ; grad */
         for (int i = 0; i < K; ++i) {
             for (int c = 0; c < D; ++c) {
@@ -253,15 +264,14 @@ int oracle_linear_chain_dual(int D, int K, int L, int64_t offset,
                 Attn[i * K + j] = acc;
             }
         /* b1_bar = b1_init - tril(eta) @ grad ;
-         * Z1_bar = XQ @ W1_init - (eta * Attn1) @ grad + b1_bar,
-         * with eta_ij = lr_j (token_eta == 1) */
+         * Z1_bar = XQ @ W1_init - (eta * Attn1) @ grad + b1_bar */
         for (int i = 0; i < K; ++i)
             for (int c = 0; c < D; ++c) {
                 double bbar = b[c];
-                for (int j = 0; j <= i; ++j) bbar -= et[j] * gZ[j * D + c];
+                for (int j = 0; j <= i; ++j) bbar -= E[i * K + j] * gZ[j * D + c];
                 double acc = 0.0;
                 for (int r = 0; r < D; ++r) acc += XQ[i * D + r] * W[r * D + c];
-                for (int j = 0; j <= i; ++j) acc -= et[j] * Attn[i * K + j] * gZ[j * D + c];
+                for (int j = 0; j <= i; ++j) acc -= E[i * K + j] * Attn[i * K + j] * gZ[j * D + c];
                 Zb[i * D + c] = acc + bbar;
             }
         /* XQW = XQ + ln_fwd(Z1_bar) */
@@ -271,21 +281,22 @@ int oracle_linear_chain_dual(int D, int K, int L, int64_t offset,
             for (int c = 0; c < D; ++c) ot[c] = XQ[i * D + c] + y[c];
         }
         /* W1_last = W1_init - (last_eta * X1)^T @ grad ;
-         * b1_last = b1_init - sum(last_eta * grad) */
+         * b1_last = b1_init - sum(last_eta * grad), last_eta = row K-1 of eta */
+        const double *le = E + (size_t)(K - 1) * K;
         for (int r = 0; r < D; ++r)
             for (int c = 0; c < D; ++c) {
                 double acc = 0.0;
-                for (int j = 0; j < K; ++j) acc += et[j] * X1[j * D + r] * gZ[j * D + c];
+                for (int j = 0; j < K; ++j) acc += le[j] * X1[j * D + r] * gZ[j * D + c];
                 W[r * D + c] -= acc;
             }
         for (int c = 0; c < D; ++c) {
             double acc = 0.0;
-            for (int j = 0; j < K; ++j) acc += et[j] * gZ[j * D + c];
+            for (int j = 0; j < K; ++j) acc += le[j] * gZ[j * D + c];
             b[c] -= acc;
         }
     }
     free(XQ); free(X1); free(Z1); free(tgt); free(gZ); free(Zb); free(Attn);
-    free(y); free(et);
+    free(y); free(E);
     return 0;
 }
 
@@ -301,10 +312,11 @@ int oracle_linear_chain_dual(int D, int K, int L, int64_t offset,
 void oracle_mlp_chain(int D, int F, int K, int L, int64_t offset,
                       const double *q, const double *k, const double *v,
                       int64_t ld, const double *eta, int64_t eta_st,
-                      const double *gamma, const double *beta, int rope,
-                      double rope_base, double eps, double *W1, double *b1,
-                      double *W2, double *b2, double *G1, double *gb1,
-                      double *G2, double *gb2, double *out, int64_t ld_out)
+                      const double *te, const double *gamma,
+                      const double *beta, int rope, double rope_base,
+                      double eps, double *W1, double *b1, double *W2,
+                      double *b2, double *G1, double *gb1, double *G2,
+                      double *gb2, double *out, int64_t ld_out)
 {
     double *qr = malloc(sizeof(double) * D), *kr = malloc(sizeof(double) * D);
     double *z1 = malloc(sizeof(double) * F), *x2 = malloc(sizeof(double) * F);
@@ -344,26 +356,27 @@ void oracle_mlp_chain(int D, int F, int K, int L, int64_t offset,
         for (int f = 0; f < F; ++f)
             for (int c = 0; c < D; ++c) G2[f * D + c] += e * x2[f] * g2[c];
         for (int c = 0; c < D; ++c) gb2[c] += e * g2[c];
-        /* prediction with the stepped parameters */
+        /* prediction with the stepped parameters (step scaled by token_eta) */
+        double tp = te ? te[pos % K] : 1.0;
         for (int f = 0; f < F; ++f) {
-            double acc = b1[f] - gb1[f];
-            for (int r = 0; r < D; ++r) acc += qr[r] * (W1[r * F + f] - G1[r * F + f]);
+            double acc = b1[f] - tp * gb1[f];
+            for (int r = 0; r < D; ++r) acc += qr[r] * (W1[r * F + f] - tp * G1[r * F + f]);
             zb1[f] = acc;
             xb2[f] = oracle_gelu(acc);
         }
         for (int c = 0; c < D; ++c) {
-            double acc = b2[c] - gb2[c];
-            for (int f = 0; f < F; ++f) acc += xb2[f] * (W2[f * D + c] - G2[f * D + c]);
+            double acc = b2[c] - tp * gb2[c];
+            for (int f = 0; f < F; ++f) acc += xb2[f] * (W2[f * D + c] - tp * G2[f * D + c]);
             zb2[c] = acc;
         }
         oracle_ln_fwd(zb2, gamma, beta, D, eps, y);
         double *ot = out + (int64_t)t * ld_out;
         for (int c = 0; c < D; ++c) ot[c] = qr[c] + y[c];
         if ((pos + 1) % K == 0) {
-            for (int i = 0; i < D * F; ++i) { W1[i] -= G1[i]; G1[i] = 0.0; }
-            for (int i = 0; i < F * D; ++i) { W2[i] -= G2[i]; G2[i] = 0.0; }
-            for (int f = 0; f < F; ++f) { b1[f] -= gb1[f]; gb1[f] = 0.0; }
-            for (int c = 0; c < D; ++c) { b2[c] -= gb2[c]; gb2[c] = 0.0; }
+            for (int i = 0; i < D * F; ++i) { W1[i] -= tp * G1[i]; G1[i] = 0.0; }
+            for (int i = 0; i < F * D; ++i) { W2[i] -= tp * G2[i]; G2[i] = 0.0; }
+            for (int f = 0; f < F; ++f) { b1[f] -= tp * gb1[f]; gb1[f] = 0.0; }
+            for (int c = 0; c < D; ++c) { b2[c] -= tp * gb2[c]; gb2[c] = 0.0; }
         }
     }
     free(qr); free(kr); free(z1); free(x2); free(z2); free(tgt); free(g2);
@@ -379,9 +392,10 @@ void oracle_mlp_chain(int D, int F, int K, int L, int64_t offset,
 int oracle_mlp_chain_dual(int D, int F, int K, int L, int64_t offset,
                           const double *q, const double *k, const double *v,
                           int64_t ld, const double *eta, int64_t eta_st,
-                          const double *gamma, const double *beta, int rope,
-                          double rope_base, double eps, double *W1, double *b1,
-                          double *W2, double *b2, double *out, int64_t ld_out)
+                          const double *te, const double *gamma,
+                          const double *beta, int rope, double rope_base,
+                          double eps, double *W1, double *b1, double *W2,
+                          double *b2, double *out, int64_t ld_out)
 {
     if (offset % K != 0 || L % K != 0) return -1;
     double *XQ = malloc(sizeof(double) * K * D), *X1 = malloc(sizeof(double) * K * D);
@@ -390,14 +404,17 @@ int oracle_mlp_chain_dual(int D, int F, int K, int L, int64_t offset,
     double *g2 = malloc(sizeof(double) * K * D), *g1 = malloc(sizeof(double) * K * F);
     double *Zb1 = malloc(sizeof(double) * K * F), *Xb2 = malloc(sizeof(double) * K * F);
     double *Zb2 = malloc(sizeof(double) * K * D), *y = malloc(sizeof(double) * D);
-    double *et = malloc(sizeof(double) * K);
+    double *E = malloc(sizeof(double) * K * K);
     for (int n = 0; n < L / K; ++n) {
         for (int i = 0; i < K; ++i) {
             int t = n * K + i;
             maybe_rope(q + (int64_t)t * ld, D, rope, offset + t, K, rope_base, XQ + i * D);
             maybe_rope(k + (int64_t)t * ld, D, rope, offset + t, K, rope_base, X1 + i * D);
-            et[i] = eta[(int64_t)t * eta_st];
         }
+        /* E_ij = token_eta_i * lr_j, as for the linear layer */
+        for (int i = 0; i < K; ++i)
+            for (int j = 0; j < K; ++j)
+                E[i * K + j] = (te ? te[i] : 1.0) * eta[(int64_t)(n * K + j) * eta_st];
         for (int i = 0; i < K; ++i) {
             for (int f = 0; f < F; ++f) {
                 double acc = b1[f];
@@ -427,7 +444,7 @@ int oracle_mlp_chain_dual(int D, int F, int K, int L, int64_t offset,
                 for (int j = 0; j <= i; ++j) {
                     double a = 1.0;
                     for (int r = 0; r < D; ++r) a += XQ[i * D + r] * X1[j * D + r];
-                    acc -= et[j] * a * g1[j * F + f];
+                    acc -= E[i * K + j] * a * g1[j * F + f];
                 }
                 Zb1[i * F + f] = acc;
                 Xb2[i * F + f] = oracle_gelu(acc);
@@ -440,7 +457,7 @@ int oracle_mlp_chain_dual(int D, int F, int K, int L, int64_t offset,
                 for (int j = 0; j <= i; ++j) {
                     double a = 1.0;
                     for (int f = 0; f < F; ++f) a += Xb2[i * F + f] * X2[j * F + f];
-                    acc -= et[j] * a * g2[j * D + c];
+                    acc -= E[i * K + j] * a * g2[j * D + c];
                 }
                 Zb2[i * D + c] = acc;
             }
@@ -449,45 +466,47 @@ int oracle_mlp_chain_dual(int D, int F, int K, int L, int64_t offset,
             double *ot = out + (int64_t)(n * K + i) * ld_out;
             for (int c = 0; c < D; ++c) ot[c] = XQ[i * D + c] + y[c];
         }
-        /* step over the whole mini-batch */
+        /* step over the whole mini-batch, with the last row of eta */
+        const double *le = E + (size_t)(K - 1) * K;
         for (int r = 0; r < D; ++r)
             for (int f = 0; f < F; ++f) {
                 double acc = 0.0;
-                for (int j = 0; j < K; ++j) acc += et[j] * X1[j * D + r] * g1[j * F + f];
+                for (int j = 0; j < K; ++j) acc += le[j] * X1[j * D + r] * g1[j * F + f];
                 W1[r * F + f] -= acc;
             }
         for (int f = 0; f < F; ++f) {
             double acc = 0.0;
-            for (int j = 0; j < K; ++j) acc += et[j] * g1[j * F + f];
+            for (int j = 0; j < K; ++j) acc += le[j] * g1[j * F + f];
             b1[f] -= acc;
         }
         for (int f = 0; f < F; ++f)
             for (int c = 0; c < D; ++c) {
                 double acc = 0.0;
-                for (int j = 0; j < K; ++j) acc += et[j] * X2[j * F + f] * g2[j * D + c];
+                for (int j = 0; j < K; ++j) acc += le[j] * X2[j * F + f] * g2[j * D + c];
                 W2[f * D + c] -= acc;
             }
         for (int c = 0; c < D; ++c) {
             double acc = 0.0;
-            for (int j = 0; j < K; ++j) acc += et[j] * g2[j * D + c];
+            for (int j = 0; j < K; ++j) acc += le[j] * g2[j * D + c];
             b2[c] -= acc;
         }
     }
     free(XQ); free(X1); free(Z1); free(X2); free(Z2); free(tgt); free(g2);
-    free(g1); free(Zb1); free(Xb2); free(Zb2); free(y); free(et);
+    free(g1); free(Zb1); free(Xb2); free(Zb2); free(y); free(E);
     return 0;
 }
 
 /* ---------------------------------------------------------------------- */
 /* Batched drivers: independent (b, h) chains, OpenMP over chains.        */
 /* Inputs [B, H, L, D] contiguous; eta [B, H, L] with batch stride        */
-/* eta_sB (0 = shared over the batch); ln params [H, D]; state arrays     */
+/* eta_sB (0 = shared over the batch); te [K] or NULL; ln params [H, D]; */
+/* state arrays                                                           */
 /* [B, H, ...] contiguous; out [B, H, L, D].  W0 tiling over the batch    */
 /* is done by the caller ([P3 TTTLinear.ttt: torch.tile of W1, b1]).      */
 /* ---------------------------------------------------------------------- */
 void oracle_linear_batch(int B, int H, int D, int K, int L, int64_t offset,
                          const double *XQ, const double *XK, const double *XV,
-                         const double *eta, int64_t eta_sB,
+                         const double *eta, int64_t eta_sB, const double *te,
                          const double *ln_w, const double *ln_b, int rope,
                          double rope_base, double eps, double *W, double *b,
                          double *G, double *gb, double *out)
@@ -498,7 +517,7 @@ void oracle_linear_batch(int B, int H, int D, int K, int L, int64_t offset,
         int64_t bi = ch / H, hi = ch % H;
         int64_t xo = ch * (int64_t)L * D;
         oracle_linear_chain(D, K, L, offset, XQ + xo, XK + xo, XV + xo, D,
-                            eta + bi * eta_sB + hi * (int64_t)L, 1,
+                            eta + bi * eta_sB + hi * (int64_t)L, 1, te,
                             ln_w + hi * D, ln_b + hi * D, rope, rope_base, eps,
                             W + ch * D * D, b + ch * D, G + ch * D * D,
                             gb + ch * D, out + xo, D);
@@ -507,8 +526,9 @@ void oracle_linear_batch(int B, int H, int D, int K, int L, int64_t offset,
 
 void oracle_mlp_batch(int B, int H, int D, int F, int K, int L, int64_t offset,
                       const double *XQ, const double *XK, const double *XV,
-                      const double *eta, int64_t eta_sB, const double *ln_w,
-                      const double *ln_b, int rope, double rope_base,
+                      const double *eta, int64_t eta_sB, const double *te,
+                      const double *ln_w, const double *ln_b, int rope,
+                      double rope_base,
                       double eps, double *W1, double *b1, double *W2,
                       double *b2, double *G1, double *gb1, double *G2,
                       double *gb2, double *out)
@@ -519,7 +539,7 @@ void oracle_mlp_batch(int B, int H, int D, int F, int K, int L, int64_t offset,
         int64_t bi = ch / H, hi = ch % H;
         int64_t xo = ch * (int64_t)L * D;
         oracle_mlp_chain(D, F, K, L, offset, XQ + xo, XK + xo, XV + xo, D,
-                         eta + bi * eta_sB + hi * (int64_t)L, 1,
+                         eta + bi * eta_sB + hi * (int64_t)L, 1, te,
                          ln_w + hi * D, ln_b + hi * D, rope, rope_base, eps,
                          W1 + ch * D * F, b1 + ch * F, W2 + ch * F * D,
                          b2 + ch * D, G1 + ch * D * F, gb1 + ch * F,

@@ -110,9 +110,12 @@ def test_rope_properties(orc):
 # ----------------------------------------------------------------------------
 # TTT-Linear: the oracle against the gradient-step definition (autograd)
 # ----------------------------------------------------------------------------
-def _linear_by_autograd(q, k, v, eta, gam, bet, W0, b0, K, offset=0, rope=False, loss_scale=0.5):
+def _linear_by_autograd(q, k, v, eta, gam, bet, W0, b0, K, offset=0, rope=False, loss_scale=0.5, token_eta=None):
     """Definition of the layer written with autograd.  Block boundaries are at
-    absolute positions that are multiples of K; ``offset`` must be aligned."""
+    absolute positions that are multiples of K; ``offset`` must be aligned.
+    token_eta[i] scales the step used by the prediction of block row i (the
+    pages' W1_bar = W1_init - grad_W1 * token_eta); the step carried to the
+    next block is that of row K - 1."""
     assert offset % K == 0
     L, D = q.shape
     T = lambda a: torch.tensor(np.asarray(a, dtype=np.float64))  # noqa: E731
@@ -130,7 +133,8 @@ def _linear_by_autograd(q, k, v, eta, gam, bet, W0, b0, K, offset=0, rope=False,
             zj = k[j] @ Wp + bp
             loss = loss + eta[j] * loss_scale * ((Fn.layer_norm(zj, (D,), gam, bet, EPS) - (v[j] - k[j])) ** 2).sum()
         gW, gb = torch.autograd.grad(loss, (Wp, bp))
-        Wbar, bbar = W - gW, b - gb
+        te = 1.0 if token_eta is None else float(token_eta[(offset + t) % K])
+        Wbar, bbar = W - te * gW, b - te * gb
         outs.append(q[t] + Fn.layer_norm(q[t] @ Wbar + bbar, (D,), gam, bet, EPS))
         if (t + 1) % K == 0:
             W, b = Wbar.detach(), bbar.detach()
@@ -150,11 +154,18 @@ def _problem(seed, L, D, rich=True):
     return q, k, v, eta, gam, bet, W0, b0
 
 
-def _run_oracle_linear(orc, q, k, v, eta, gam, bet, W0, b0, K, offset=0, rope=False):
+def _run_oracle_linear(orc, q, k, v, eta, gam, bet, W0, b0, K, offset=0, rope=False, token_eta=None):
     D = q.shape[1]
     W, b, G, gb = W0.copy(), b0.copy(), np.zeros((D, D)), np.zeros(D)
-    out = orc.linear_chain(q, k, v, eta, gam, bet, W, b, G, gb, K=K, offset=offset, rope=rope)
+    out = orc.linear_chain(q, k, v, eta, gam, bet, W, b, G, gb, K=K, offset=offset, rope=rope, token_eta=token_eta)
     return out, W, b, G, gb
+
+
+def _token_eta(K, seed):
+    """A non-constant token_eta: 1/(i+1) (the usual choice for this factor)
+    perturbed, so no two rows share a value."""
+    r = _rng(seed)
+    return 1.0 / np.arange(1, K + 1) + 0.05 * r.uniform(size=K)
 
 
 @pytest.mark.parametrize("D,K,L,rope", [(8, 4, 11, False), (16, 1, 7, False), (64, 16, 40, False),
@@ -214,6 +225,62 @@ def test_eta_zero_closed_form(orc):
     np.testing.assert_array_equal(b, b0)
 
 
+@pytest.mark.parametrize("D,K,L,rope", [(8, 4, 11, False), (64, 16, 40, True), (16, 1, 6, False)])
+def test_token_eta_matches_gradient_step_definition(orc, D, K, L, rope):
+    """token_eta scales each row's step (and the carried step is the last
+    row's): the oracle against the autograd definition with that scale."""
+    prob = _problem(500 + D * K + L, L, D)
+    te = _token_eta(K, D + L)
+    out, W, b, _, _ = _run_oracle_linear(orc, *prob, K=K, rope=rope, token_eta=te)
+    ref, Wr, br = _linear_by_autograd(*prob, K=K, rope=rope, token_eta=te)
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(W, Wr, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(b, br, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("dual", [False, True])
+def test_constant_token_eta_equals_scaled_learning_rate(orc, dual):
+    """eta_ij = token_eta_i * lr_j: a constant token_eta c is the same layer
+    as token_eta = 1 with every learning rate times c."""
+    D, K, L, c = 16, 4, 16, 0.37
+    q, k, v, eta, gam, bet, W0, b0 = _problem(61, L, D)
+    res = []
+    for te, e in ((np.full(K, c), eta), (None, c * eta)):
+        W, b = W0.copy(), b0.copy()
+        if dual:
+            o = orc.linear_chain_dual(q, k, v, e, gam, bet, W, b, K=K, token_eta=te)
+        else:
+            o = orc.linear_chain(q, k, v, e, gam, bet, W, b, np.zeros((D, D)), np.zeros(D), K=K, token_eta=te)
+        res.append((o, W, b))
+    for a, b_ in zip(*res):
+        np.testing.assert_allclose(a, b_, rtol=1e-12, atol=1e-14)
+
+
+def test_token_eta_on_last_row_only(orc):
+    """token_eta = (0, ..., 0, 1): rows before the last predict with the
+    block-start state (q + LN(q W_s + b_s)); the last row and the carried state
+    are those of token_eta = 1.  A scale applied per key token instead of per
+    output row would change the last row and the step."""
+    D, K, L = 16, 4, 12
+    q, k, v, eta, gam, bet, W0, b0 = _problem(62, L, D)
+    te = np.zeros(K)
+    te[-1] = 1.0
+    out, W, b, _, _ = _run_oracle_linear(orc, q, k, v, eta, gam, bet, W0, b0, K=K, token_eta=te)
+    ref, Wr, br, _, _ = _run_oracle_linear(orc, q, k, v, eta, gam, bet, W0, b0, K=K)
+    np.testing.assert_allclose(W, Wr, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(b, br, rtol=1e-13, atol=1e-15)
+    T = torch.tensor
+    for n in range(L // K):
+        Ws, bs = W0.copy(), b0.copy()
+        if n:
+            _, Ws, bs, _, _ = _run_oracle_linear(orc, q[:n * K], k[:n * K], v[:n * K], eta[:n * K], gam, bet, W0,
+                                                 b0, K=K)
+        rows = slice(n * K, n * K + K - 1)
+        closed = q[rows] + Fn.layer_norm(T(q[rows] @ Ws + bs), (D,), T(gam), T(bet), EPS).numpy()
+        np.testing.assert_allclose(out[rows], closed, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(out[n * K + K - 1], ref[n * K + K - 1], rtol=1e-12, atol=1e-12)
+
+
 @pytest.mark.parametrize("D,K,L,rope", [(8, 4, 16, False), (64, 16, 64, False), (64, 16, 48, True),
                                          (16, 1, 5, False), (8, 3, 12, True)])
 def test_dual_equals_primal(orc, D, K, L, rope):
@@ -224,6 +291,33 @@ def test_dual_equals_primal(orc, D, K, L, rope):
     np.testing.assert_allclose(out_d, out_p, rtol=1e-11, atol=1e-11)
     np.testing.assert_allclose(Wd, Wp, rtol=1e-11, atol=1e-13)
     np.testing.assert_allclose(bd, bp, rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("D,K,L,rope", [(8, 4, 16, False), (64, 16, 48, True)])
+def test_dual_equals_primal_token_eta(orc, D, K, L, rope):
+    """The dual branch with eta_ij = token_eta_i * lr_j (its [K, K] eta and
+    the last row for the step) against the primal per-token form."""
+    q, k, v, eta, gam, bet, W0, b0 = _problem(19 + L, L, D)
+    te = _token_eta(K, L)
+    out_p, Wp, bp, _, _ = _run_oracle_linear(orc, q, k, v, eta, gam, bet, W0, b0, K=K, rope=rope, token_eta=te)
+    Wd, bd = W0.copy(), b0.copy()
+    out_d = orc.linear_chain_dual(q, k, v, eta, gam, bet, Wd, bd, K=K, rope=rope, token_eta=te)
+    np.testing.assert_allclose(out_d, out_p, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(Wd, Wp, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(bd, bp, rtol=1e-11, atol=1e-13)
+
+
+def test_split_invariance_every_cut_token_eta(orc):
+    D, K, L = 16, 8, 40
+    q, k, v, eta, gam, bet, W0, b0 = _problem(43, L, D)
+    te = _token_eta(K, 5)
+    whole, Ww, bw, _, _ = _run_oracle_linear(orc, q, k, v, eta, gam, bet, W0, b0, K=K, token_eta=te)
+    for s in range(1, L):
+        W, b, G, gb = W0.copy(), b0.copy(), np.zeros((D, D)), np.zeros(D)
+        o1 = orc.linear_chain(q[:s], k[:s], v[:s], eta[:s], gam, bet, W, b, G, gb, K=K, token_eta=te)
+        o2 = orc.linear_chain(q[s:], k[s:], v[s:], eta[s:], gam, bet, W, b, G, gb, K=K, offset=s, token_eta=te)
+        np.testing.assert_allclose(np.concatenate([o1, o2]), whole, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(W, Ww, rtol=1e-12, atol=1e-14)
 
 
 @pytest.mark.parametrize("rope", [False, True])
@@ -298,14 +392,14 @@ def _mlp_problem(seed, L, D, F):
     return q, k, v, eta, gam, bet, W1, b1, W2, b2
 
 
-def _run_oracle_mlp(orc, q, k, v, eta, gam, bet, W1, b1, W2, b2, K, offset=0, rope=False):
+def _run_oracle_mlp(orc, q, k, v, eta, gam, bet, W1, b1, W2, b2, K, offset=0, rope=False, token_eta=None):
     D, F = W1.shape
     st = [W1.copy(), b1.copy(), W2.copy(), b2.copy(), np.zeros((D, F)), np.zeros(F), np.zeros((F, D)), np.zeros(D)]
-    out = orc.mlp_chain(q, k, v, eta, gam, bet, *st, K=K, offset=offset, rope=rope)
+    out = orc.mlp_chain(q, k, v, eta, gam, bet, *st, K=K, offset=offset, rope=rope, token_eta=token_eta)
     return out, st
 
 
-def _mlp_by_autograd(q, k, v, eta, gam, bet, W1, b1, W2, b2, K):
+def _mlp_by_autograd(q, k, v, eta, gam, bet, W1, b1, W2, b2, K, token_eta=None):
     L, D = q.shape
     T = lambda a: torch.tensor(np.asarray(a, dtype=np.float64))  # noqa: E731
     q, k, v, eta, gam, bet = map(T, (q, k, v, eta, gam, bet))
@@ -322,7 +416,8 @@ def _mlp_by_autograd(q, k, v, eta, gam, bet, W1, b1, W2, b2, K):
         for j in range(j0, t + 1):
             loss = loss + eta[j] * 0.5 * ((Fn.layer_norm(f(k[j], Pp), (D,), gam, bet, EPS) - (v[j] - k[j])) ** 2).sum()
         grads = torch.autograd.grad(loss, Pp)
-        Pbar = [p - g for p, g in zip(P, grads)]
+        te = 1.0 if token_eta is None else float(token_eta[t % K])
+        Pbar = [p - te * g for p, g in zip(P, grads)]
         outs.append(q[t] + Fn.layer_norm(f(q[t], Pbar), (D,), gam, bet, EPS))
         if (t + 1) % K == 0:
             P = [p.detach() for p in Pbar]
@@ -337,6 +432,29 @@ def test_mlp_matches_gradient_step_definition(orc, D, F, K, L):
     np.testing.assert_allclose(out, ref, rtol=1e-9, atol=1e-10)
     for a, b in zip(st[:4], Pr):
         np.testing.assert_allclose(a, b, rtol=1e-9, atol=1e-12)
+
+
+@pytest.mark.parametrize("D,F,K,L", [(8, 16, 4, 10), (64, 256, 16, 32)])
+def test_mlp_token_eta_matches_gradient_step_definition(orc, D, F, K, L):
+    prob = _mlp_problem(7 + D + F + L, L, D, F)
+    te = _token_eta(K, F)
+    out, st = _run_oracle_mlp(orc, *prob, K=K, token_eta=te)
+    ref, Pr = _mlp_by_autograd(*prob, K=K, token_eta=te)
+    np.testing.assert_allclose(out, ref, rtol=1e-9, atol=1e-10)
+    for a, b in zip(st[:4], Pr):
+        np.testing.assert_allclose(a, b, rtol=1e-9, atol=1e-12)
+
+
+@pytest.mark.parametrize("D,F,K,L", [(8, 16, 4, 12), (64, 256, 16, 32)])
+def test_mlp_dual_equals_primal_token_eta(orc, D, F, K, L):
+    q, k, v, eta, gam, bet, W1, b1, W2, b2 = _mlp_problem(15 + L, L, D, F)
+    te = _token_eta(K, D)
+    out_p, st = _run_oracle_mlp(orc, q, k, v, eta, gam, bet, W1, b1, W2, b2, K=K, token_eta=te)
+    sd = [W1.copy(), b1.copy(), W2.copy(), b2.copy()]
+    out_d = orc.mlp_chain_dual(q, k, v, eta, gam, bet, *sd, K=K, token_eta=te)
+    np.testing.assert_allclose(out_d, out_p, rtol=1e-10, atol=1e-11)
+    for a, b in zip(sd, st[:4]):
+        np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-13)
 
 
 @pytest.mark.parametrize("D,F,K,L,rope", [(8, 16, 4, 12, False), (64, 256, 16, 32, True)])

@@ -31,8 +31,10 @@
  *  - LN uses the population variance with eps inside the square root;
  *    gamma/beta are per head ("ttt_norm_weight/bias" reshaped per head);
  *  - the loss is half the squared error;
- *  - eta_ij = token_eta_i * lr_j with token_eta = 1: one learning rate per
- *    key token, the causal mask includes the diagonal;
+ *  - eta_ij = token_eta_i * lr_j: lr_j is the learning rate of key token j,
+ *    token_eta_i scales the step seen by output row i of the mini-batch and
+ *    the step carried at the boundary is that of the last row (token_eta is
+ *    optional, all ones by default); the causal mask includes the diagonal;
  *  - rotary embedding pairs dimension i with i + D/2, angle
  *    p * base^(-2i/D), p = absolute position mod K; applied to q and k only,
  *    before everything else (target and residual use the rotated values);
@@ -93,12 +95,22 @@ typedef struct ttt_tensor {
     int64_t sB, sH, sL;
 } ttt_tensor;
 
-/* Learning rates eta[b, h, t] (fp32, token stride 1); sB = 0 shares them over
- * the batch.  Row t of the block holds the rate of key token t
- * ("ttt_lr_eta" in compute_mini_batch). */
+/* Learning rates.
+ *  data:      eta[b, h, t] (fp32, token stride 1); sB = 0 shares them over
+ *             the batch.  The rate of key token t ("ttt_lr_eta" in
+ *             compute_mini_batch).
+ *  token_eta: NULL, or K fp32 values (device, 16-byte aligned): the scale of
+ *             the step seen by the token at position i (mod K) of its
+ *             mini-batch ("token_eta" in compute_mini_batch: the primal
+ *             branch's W1_bar = W1_init - grad_W1 * token_eta, the dual
+ *             branch's eta_ij = token_eta_i * lr_j).  The step committed at
+ *             a mini-batch boundary is that of the last position,
+ *             token_eta[K-1] * sum_j lr_j k_j^T g_j.  NULL means all ones.
+ *             The same values for every batch and head. */
 typedef struct ttt_eta {
     const float *data;
     int64_t sB, sH;
+    const float *token_eta;
 } ttt_eta;
 
 typedef struct ttt_linear_cfg {

@@ -40,6 +40,7 @@ struct LinearArgs {
     float rope_base;
     float eps;
     int32_t grad_rows;          // W_grad holds the open mini-batch's rows [k_j | eta_j g_j]
+    const float *te;            // token_eta [K] or nullptr (all ones)
 };
 
 __device__ __forceinline__ float to_f32(float x) { return x; }

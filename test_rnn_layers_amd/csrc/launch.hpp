@@ -24,6 +24,7 @@ struct MlpArgs {
     int32_t rope;
     float rope_base;
     float eps;
+    const float *te;  // token_eta [16] or nullptr (all ones)
 };
 
 hipError_t launch_linear_token(const LinearArgs &a, int in_bf16, int out_bf16, hipStream_t s);

@@ -2,14 +2,16 @@
 // ("代码连连看——TTT", compute_mini_batch, dual branch; "TTTLinear.ttt": the
 // scan over mini-batches carrying W, b).
 //
-// Per mini-batch n of 16 tokens (rows of Q_n, K_n, V_n; eta_j per key token):
+// Per mini-batch n of 16 tokens (rows of Q_n, K_n, V_n; eta_j per key token;
+// t_i = token_eta of row i, t = t_15 the last row's):
 //   Z_n    = K_n W_n + b_n                          (16x64x64)
 //   g      = d/dZ of 1/2 ||LN(Z_n) - (V_n - K_n)||^2, row by row
 //   ng_n   = -eta_j g_j                             (rows scaled and negated)
-//   Zbar_n = Q_n W_n + b_n + tril(Q_n K_n^T + 1) ng_n
-//            (the pages' Attn1 and b1_bar folded into one 16x16x64 product)
+//   Zbar_n = Q_n W_n + b_n + diag(t_i) tril(Q_n K_n^T + 1) ng_n
+//            (the pages' Attn1 and b1_bar folded into one 16x16x64 product,
+//            their [K, K] eta being t_i eta_j)
 //   out_n  = Q_n + LN(Zbar_n)
-//   W_n+1  = W_n + K_n^T ng_n ,  b_n+1 = b_n + 1^T ng_n   (W1_last, b1_last)
+//   W_n+1  = W_n + t K_n^T ng_n ,  b_n+1 = b_n + t 1^T ng_n  (W1_last, b1_last)
 //
 // Design (gfx950, one persistent workgroup of 8 waves per (batch, head)):
 //  * Column waves 0..3: wave c owns the 64x16 slab W[:, 16c..16c+15] as four
@@ -21,12 +23,12 @@
 //    LayerNorm backward (-> ng, to LDS as MFMA B fragments) and forward
 //    (-> out, stored to HBM) with DPP row reductions.
 //  * Look-ahead on the sequential chain:
-//      Z_n+1 = K_n+1 W_n + b_n + (K_n+1 K_n^T + 1) ng_n,
+//      Z_n+1 = K_n+1 W_n + b_n + t (K_n+1 K_n^T + 1) ng_n,
 //    the first term formed while ng_n is being computed, so each mini-batch
 //    costs one 16x16x16 product, one LayerNorm backward and two barriers on
 //    the critical path.  The two wave roles share each SIMD and overlap.
-//  * K^T fragments for the state step come from an MFMA of K against a 0/1
-//    selection pattern (exact), instead of a transposed copy in LDS.
+//  * K^T fragments for the state step come from an MFMA of K against a 0/t
+//    selection pattern (exact for t = 1), instead of a transposed copy in LDS.
 //  * Operands: bf16 inputs run the products on fp16 MFMA (inputs, W, ng and
 //    the 16x16 matrices rounded to fp16; fp32 accumulation); fp32 inputs run
 //    them on fp32 MFMA.
@@ -67,7 +69,7 @@ struct Op<_Float16> {
         return F4{G[(4 * g) * GP + col], G[(4 * g + 1) * GP + col], G[(4 * g + 2) * GP + col],
                   G[(4 * g + 3) * GP + col]};
     }
-    // selection patterns for K^T: element i of pattern h is 1 where slot
+    // selection patterns for K^T: element i of pattern h is t where slot
     // 8g+i carries column 16r + n of the output tile (r = 2s + h)
     struct Sel {
         h8 p[2];
@@ -104,13 +106,13 @@ struct Op<_Float16> {
         return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, acc, 0, 0, 0);
     }
     __device__ static F4 make(f32x4 x) { return F4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]}; }
-    __device__ static Sel sel(int n, int g) {
+    __device__ static Sel sel(int n, int g, float t) {
         Sel s;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                s.p[h][i] = (i / 4 == h && 4 * g + (i & 3) == n) ? (_Float16)1.f : (_Float16)0.f;
+                s.p[h][i] = (i / 4 == h && 4 * g + (i & 3) == n) ? (_Float16)t : (_Float16)0.f;
         return s;
     }
     // tile r of K (rows = tokens, columns 16r..16r+15) in accumulator layout,
@@ -141,7 +143,7 @@ struct Op<float> {
                   G[(4 * g + 3) * GP + col]};
     }
     struct Sel {
-        float p[4];  // p[j] = 1 where 4g + j == n
+        float p[4];  // p[j] = t where 4g + j == n
     };
     __device__ static XF load_x(const float *X, int n, int g) {
         XF x;
@@ -170,10 +172,10 @@ struct Op<float> {
         return acc;
     }
     __device__ static F4 make(f32x4 x) { return x; }
-    __device__ static Sel sel(int n, int g) {
+    __device__ static Sel sel(int n, int g, float t) {
         Sel s;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) s.p[j] = (4 * g + j == n) ? 1.f : 0.f;
+        for (int j = 0; j < 4; ++j) s.p[j] = (4 * g + j == n) ? t : 0.f;
         return s;
     }
     __device__ static void kt_frags(const XF &k, const Sel &s, F4 (&kt)[4]) {
@@ -539,15 +541,22 @@ __device__ void row_main(const LinearArgs &a, Smem<T> &sm, int bi, int hi, int r
     }
 }
 
-// causal matrix tril(S + 1) from S^T in accumulator layout (lane: query n, keys 4g+j)
-__device__ __forceinline__ f32x4 causal(f32x4 st, int n, int g) {
+// causal matrix t_n tril(S + 1) from S^T in accumulator layout (lane: query
+// n, keys 4g+j; t_n the query row's token_eta)
+__device__ __forceinline__ f32x4 causal(f32x4 st, int n, int g, float tn) {
     f32x4 m;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) m[j] = (4 * g + j <= n) ? st[j] + 1.f : 0.f;
+    for (int j = 0; j < 4; ++j) m[j] = (4 * g + j <= n) ? fmaf(st[j], tn, tn) : 0.f;
     return m;
 }
 
-template <typename T>
+__device__ __forceinline__ f32x4 scaled(f32x4 x, float t) {
+    return f32x4{x[0] * t, x[1] * t, x[2] * t, x[3] * t};
+}
+
+// TE: token_eta given (otherwise every scale is the constant 1 and the code is
+// that of the plain dual form)
+template <typename T, bool TE>
 __device__ void col_main(const LinearArgs &a, Smem<T> &sm, int ch, int c, int g, int n) {
     using O = Op<T>;
     using F4 = typename O::F4;
@@ -565,13 +574,16 @@ __device__ void col_main(const LinearArgs &a, Smem<T> &sm, int ch, int c, int g,
         const float bv = a.b[(int64_t)ch * kD + 16 * c + n];
         Bt = f32x4{bv, bv, bv, bv};
     }
-    const typename O::Sel sel = O::sel(n, g);
-    const F4 ones = O::make(f32x4{1.f, 1.f, 1.f, 1.f});
+    // token_eta of query row n, and of the last row (the carried step)
+    const float tn = TE ? a.te[n] : 1.f;
+    const float tl = TE ? a.te[kM - 1] : 1.f;
+    const typename O::Sel sel = O::sel(n, g, tl);
+    const F4 ones = O::make(f32x4{tl, tl, tl, tl});
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f}, one = {1.f, 1.f, 1.f, 1.f};
 
     f32x4 Y, P;   // Y_m+1 = K_m+1 W_m + b_m ; P_m = Q_m W_m + b_m
-    F4 Mf, Cf;    // tril(Q_m K_m^T + 1), K_m+1 K_m^T + 1 (A fragments)
-    F4 kt[4];     // K_m^T rows 16r .. 16r+15 (A fragments)
+    F4 Mf, Cf;    // t_i tril(Q_m K_m^T + 1), t (K_m+1 K_m^T + 1) (A fragments)
+    F4 kt[4];     // t K_m^T rows 16r .. 16r+15 (A fragments)
     XF kxn;       // K_m row fragment
 
     phase_barrier();  // mini-batches 0, 1 staged
@@ -583,10 +595,10 @@ __device__ void col_main(const LinearArgs &a, Smem<T> &sm, int ch, int c, int g,
 #pragma unroll
         for (int j = 0; j < 4; ++j) sm.zbuf[4 * g + j][16 * c + n] = Z0[j];
         P = O::xx(qx0, wf, Bt);
-        Mf = O::make(causal(O::xx(kx0, qx0, zero), n, g));
+        Mf = O::make(causal(O::xx(kx0, qx0, zero), n, g, tn));
         const XF kx1 = O::load_x(&sm.st[1].kx[0][0], n, g);
         Y = O::xx(kx1, wf, Bt);
-        Cf = O::make(O::xx(kx0, kx1, one));
+        Cf = O::make(scaled(O::xx(kx0, kx1, one), tl));
         O::kt_frags(kx0, sel, kt);
         kxn = kx1;
     }
@@ -616,8 +628,8 @@ __device__ void col_main(const LinearArgs &a, Smem<T> &sm, int ch, int c, int g,
         const XF kx1 = O::load_x(&sm.st[(m + 1) % kRing].kx[0][0], n, g);  // stale past the end: unused
         P = O::xx(qx, wf, Bt);
         Y = O::xx(kx1, wf, Bt);
-        Mf = O::make(causal(O::xx(kxn, qx, zero), n, g));
-        Cf = O::make(O::xx(kxn, kx1, one));
+        Mf = O::make(causal(O::xx(kxn, qx, zero), n, g, tn));
+        Cf = O::make(scaled(O::xx(kxn, kx1, one), tl));
         O::kt_frags(kxn, sel, kt);
         kxn = kx1;
         phase_barrier();  // ng_m ready, Zbar_m-1 written
@@ -646,7 +658,7 @@ __device__ void col_main(const LinearArgs &a, Smem<T> &sm, int ch, int c, int g,
 template <typename T>
 constexpr int kWavesPerSimd = std::is_same<T, _Float16>::value ? 4 : 1;
 
-template <typename Tin, typename Tout, typename T, bool ROPE>
+template <typename Tin, typename Tout, typename T, bool ROPE, bool TE>
 __global__ __launch_bounds__(512, kWavesPerSimd<T>) void linear_dual_kernel(LinearArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Smem<T> &sm = *reinterpret_cast<Smem<T> *>(smem_raw);
@@ -655,14 +667,14 @@ __global__ __launch_bounds__(512, kWavesPerSimd<T>) void linear_dual_kernel(Line
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, n = l & 15;
     // both roles pass the same sequence of 2N + 2 barriers
     if (w < 4)
-        col_main<T>(a, sm, ch, w, g, n);
+        col_main<T, TE>(a, sm, ch, w, g, n);
     else
         row_main<Tin, Tout, T, ROPE>(a, sm, bi, hi, w - 4, g, n);
 }
 
-template <typename Tin, typename Tout, typename T, bool ROPE>
+template <typename Tin, typename Tout, typename T, bool ROPE, bool TE>
 hipError_t launch_typed(const LinearArgs &a, hipStream_t s) {
-    const void *fn = (const void *)&linear_dual_kernel<Tin, Tout, T, ROPE>;
+    const void *fn = (const void *)&linear_dual_kernel<Tin, Tout, T, ROPE, TE>;
     const size_t lds = sizeof(Smem<T>);
     static bool configured = false;  // per instantiation
     if (!configured) {
@@ -670,13 +682,15 @@ hipError_t launch_typed(const LinearArgs &a, hipStream_t s) {
         if (e != hipSuccess) return e;
         configured = true;
     }
-    hipLaunchKernelGGL((linear_dual_kernel<Tin, Tout, T, ROPE>), dim3(a.B * a.H), dim3(512), lds, s, a);
+    hipLaunchKernelGGL((linear_dual_kernel<Tin, Tout, T, ROPE, TE>), dim3(a.B * a.H), dim3(512), lds, s, a);
     return hipGetLastError();
 }
 
 template <typename Tin, typename Tout, typename T>
 hipError_t launch_rope(const LinearArgs &a, hipStream_t s) {
-    return a.rope ? launch_typed<Tin, Tout, T, true>(a, s) : launch_typed<Tin, Tout, T, false>(a, s);
+    if (a.te != nullptr)
+        return a.rope ? launch_typed<Tin, Tout, T, true, true>(a, s) : launch_typed<Tin, Tout, T, false, true>(a, s);
+    return a.rope ? launch_typed<Tin, Tout, T, true, false>(a, s) : launch_typed<Tin, Tout, T, false, false>(a, s);
 }
 
 }  // namespace

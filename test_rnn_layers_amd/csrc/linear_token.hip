@@ -4,9 +4,11 @@
 // Primal form of "代码连连看——TTT", compute_mini_batch, primal branch: for
 // each token the gradient of its LN + L2 reconstruction loss is taken at the
 // mini-batch-start W, b; the eta-weighted gradients accumulate into W_grad,
-// b_grad (the pages' carried "W1_grad", "b1_grad"); the prediction uses
-// W - W_grad, b - b_grad; at a mini-batch boundary the step is committed and
-// the gradients cleared (TTTCache continuation, "TTTLinear.ttt").
+// b_grad (the pages' carried "W1_grad", "b1_grad"); the prediction of the
+// token at position p of its mini-batch uses W - token_eta_p W_grad,
+// b - token_eta_p b_grad ("W1_bar"); at a mini-batch boundary the step of the
+// last position is committed and the gradients cleared (TTTCache
+// continuation, "TTTLinear.ttt").
 //
 // One wave per (batch, head) chain.  Lane c owns column c of W and W_grad
 // for all 64 rows, in registers for the whole call, so a call over T tokens
@@ -89,6 +91,8 @@ __global__ __launch_bounds__(64, 2) void linear_token_kernel(LinearArgs a) {
         }
     }
     TokIn nxt = load_tok(a.t0);
+    // token_eta of position c of the mini-batch (lanes c < K), 1 without it
+    const float te_c = (a.te != nullptr && c < K) ? a.te[c] : 1.f;
     float bs = a.b[(int64_t)ch * kD + c];
     float gbs = g_clear ? 0.f : a.bg[(int64_t)ch * kD + c];
     const float gam = a.ln_w[hi * kD + c];
@@ -130,6 +134,9 @@ __global__ __launch_bounds__(64, 2) void linear_token_kernel(LinearArgs a) {
         const int64_t pos = a.pos0 + t;
         const int p = (int)(pos % K);  // row of this token in its mini-batch
         const TokIn in = nxt;
+        // the step this token's prediction sees, and the step committed at
+        // the end of the mini-batch, are scaled by token_eta of its position
+        const float tp = lane_value(te_c, p);
         // the next token's inputs load during this token (the last token
         // reloads its own: no branch in the loop)
         nxt = load_tok(t + 1 < a.ntok ? tok + 1 : tok);
@@ -205,7 +212,7 @@ __global__ __launch_bounds__(64, 2) void linear_token_kernel(LinearArgs a) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) qg4[j & 3] = fmaf(lane_value(sj, j), er[j][c], qg4[j & 3]);
             const float qg = (qg4[0] + qg4[1]) + (qg4[2] + qg4[3]);
-            zb = (((zq4[0] + zq4[1]) + (zq4[2] + zq4[3])) - qg) + (bs - gbs);
+            zb = fmaf(-tp, qg, (zq4[0] + zq4[1]) + (zq4[2] + zq4[3])) + fmaf(-tp, gbs, bs);
         } else {
             float zb4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -215,10 +222,10 @@ __global__ __launch_bounds__(64, 2) void linear_token_kernel(LinearArgs a) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     Gs[i + j] = fmaf(k4[j], eg, Gs[i + j]);
-                    zb4[j] = fmaf(q4[j], Ws[i + j] - Gs[i + j], zb4[j]);
+                    zb4[j] = fmaf(q4[j], fmaf(-tp, Gs[i + j], Ws[i + j]), zb4[j]);
                 }
             }
-            zb = ((zb4[0] + zb4[1]) + (zb4[2] + zb4[3])) + (bs - gbs);
+            zb = ((zb4[0] + zb4[1]) + (zb4[2] + zb4[3])) + fmaf(-tp, gbs, bs);
         }
         float t1 = zb, t2 = zb * zb;
         wave_sum2(t1, t2);
@@ -242,15 +249,15 @@ __global__ __launch_bounds__(64, 2) void linear_token_kernel(LinearArgs a) {
                     }
                 }
 #pragma unroll
-                for (int i = 0; i < kD; ++i) Ws[i] -= acc[i];
+                for (int i = 0; i < kD; ++i) Ws[i] = fmaf(-tp, acc[i], Ws[i]);
             } else {
 #pragma unroll
                 for (int i = 0; i < kD; ++i) {
-                    Ws[i] -= Gs[i];
+                    Ws[i] = fmaf(-tp, Gs[i], Ws[i]);
                     Gs[i] = 0.f;
                 }
             }
-            bs -= gbs;
+            bs = fmaf(-tp, gbs, bs);
             gbs = 0.f;
             committed = true;
         }

@@ -3,13 +3,14 @@
 // The hidden state is a two-layer MLP f(x) = GELU(x W1 + b1) W2 + b2
 // (D = 64 -> F = 256 -> D), the TTT-Linear step applied to each layer
 // ("代码连连看——TTT": TTT-MLP is TTT-Linear stacked twice; README: the hidden
-// state of TTT-MLP is a two-layer MLP).  Per mini-batch (K rows X = k, Q, V):
+// state of TTT-MLP is a two-layer MLP).  Per mini-batch (K rows X = k, Q, V;
+// T = diag(token_eta_i), t = token_eta of the last row):
 //   Z1 = X W1 + b1, X2 = GELU(Z1), Z2 = X2 W2 + b2
 //   ng2 = -eta * d/dZ2 of 1/2 ||LN(Z2) - (V - X)||^2
 //   ng1 = (ng2 W2^T) o GELU'(Z1)
-//   Zb1 = Q W1 + b1 + tril(Q X^T + 1) ng1,  Xb2 = GELU(Zb1)
-//   Zb2 = Xb2 W2 + b2 + tril(Xb2 X2^T + 1) ng2,  out = Q + LN(Zb2)
-//   W1 += X^T ng1, b1 += 1^T ng1, W2 += X2^T ng2, b2 += 1^T ng2
+//   Zb1 = Q W1 + b1 + T tril(Q X^T + 1) ng1,  Xb2 = GELU(Zb1)
+//   Zb2 = Xb2 W2 + b2 + T tril(Xb2 X2^T + 1) ng2,  out = Q + LN(Zb2)
+//   W1 += t X^T ng1, b1 += t 1^T ng1, W2 += t X2^T ng2, b2 += t 1^T ng2
 // A trailing partial mini-batch (r < 16 tokens) runs with eta = 0 on the
 // missing rows; its step is not applied: the accumulated gradients go to
 // the *_grad state instead (an open mini-batch).
@@ -294,6 +295,10 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) gam2r[e] = sm.gam2[4 * n + e];
     const h4 ones = h4{(_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f};
+    // token_eta of query row n, and of the last row (the committed step)
+    const float tn = a.te != nullptr ? a.te[n] : 1.f;
+    const float tl = a.te != nullptr ? a.te[kM - 1] : 1.f;
+    const h4 onesl = h4{(_Float16)tl, (_Float16)tl, (_Float16)tl, (_Float16)tl};
     // the 16x16 identity as a B fragment (lane: I[4g+j][n])
     h4 ident;
 #pragma unroll
@@ -330,7 +335,7 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
             const f32x4 st = mfma32(xp1, qp1, mfma32(xp0, qp0, zero));  // lane: S[query n][key 4g+j]
             f32x4 m;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) m[j] = (4 * g + j <= n) ? st[j] + 1.f : 0.f;
+            for (int j = 0; j < 4; ++j) m[j] = (4 * g + j <= n) ? fmaf(st[j], tn, tn) : 0.f;
             M1 = to_h4(m);
         }
         if (nb > 0 && threadIdx.x < kD) sm.b2[threadIdx.x] = sm.b2n[threadIdx.x];  // previous step
@@ -413,20 +418,24 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
             x2h[s] = to_h4(X2[s]);
             n1k[s] = n1;
             if (!open) {
-                // W1 += X^T ng1, with K^T rows 16r .. 16r+15 as A fragments
+                // W1 += t X^T ng1, with K^T rows 16r .. 16r+15 as A fragments
                 // (lane: K[4g+j][16r+n], from the transposed copy)
+                const h4 n1t = a.te != nullptr ? to_h4(f32x4{ng1[0] * tl, ng1[1] * tl, ng1[2] * tl, ng1[3] * tl})
+                                               : n1;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    W1s[s][r] = mfma16(*(const h4 *)&sm.kT[buf][16 * r + n][4 * g], n1, W1s[s][r]);
-                b1t[s] = mfma16(ones, n1, b1t[s]);
+                    W1s[s][r] = mfma16(*(const h4 *)&sm.kT[buf][16 * r + n][4 * g], n1t, W1s[s][r]);
+                b1t[s] = mfma16(ones, n1t, b1t[s]);
             }
         }
         if (w == 0) {
-            // b2 after the step: b2 + column sums of ng2
+            // b2 after the step: b2 + t (column sums of ng2); an open block
+            // keeps the unscaled sums (its accumulated gradient)
+            const h4 ob = open ? ones : onesl;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float bv = sm.b2[16 * r + n];
-                const f32x4 bn = mfma16(ones, G2[r], f32x4{bv, bv, bv, bv});
+                const f32x4 bn = mfma16(ob, G2[r], f32x4{bv, bv, bv, bv});
                 if (g == 0) sm.b2n[16 * r + n] = bn[0];
             }
         }
@@ -441,7 +450,7 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
             const f32x4 st = mfma32(x2p, xb2p, zero);  // lane: S[query n][key 4g+j] over the slice
             f32x4 mm;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) mm[j] = (4 * g + j <= n) ? st[j] + (w == 0 ? 1.f : 0.f) : 0.f;
+            for (int j = 0; j < 4; ++j) mm[j] = (4 * g + j <= n) ? fmaf(st[j], tn, w == 0 ? tn : 0.f) : 0.f;
             const h4 M2 = to_h4(mm);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -450,12 +459,16 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
                 for (int j = 0; j < 4; ++j) sm.part[w][4 * g + j][16 * r + n] = z[j];
             }
         }
-        // step of W2 (W2 += X2^T ng2), after its last use at the block start
+        // step of W2 (W2 += t X2^T ng2), after its last use at the block start
         if (!open) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
+            for (int s = 0; s < 2; ++s) {
+                const h4 x2t = a.te != nullptr
+                                   ? to_h4(f32x4{X2[s][0] * tl, X2[s][1] * tl, X2[s][2] * tl, X2[s][3] * tl})
+                                   : x2h[s];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) W2s[s][r] = mfma16(x2h[s], G2[r], W2s[s][r]);
+                for (int r = 0; r < 4; ++r) W2s[s][r] = mfma16(x2t, G2[r], W2s[s][r]);
+            }
         }
         phase_barrier();  // B5
 

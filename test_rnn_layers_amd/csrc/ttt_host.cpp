@@ -111,7 +111,7 @@ struct Act {
 
 // Checks everything shared by the linear and MLP calls.  `state_ranges` are
 // the device ranges of the state, which `out` must not overlap.
-ttt_status check_acts(const Act &x, int B, int H, int L, int D, int32_t in_dt, int32_t out_dt,
+ttt_status check_acts(const Act &x, int B, int H, int L, int D, int K, int32_t in_dt, int32_t out_dt,
                       const std::vector<Range> &state_ranges) {
     const size_t ei = dtype_size(in_dt), eo = dtype_size(out_dt);
     ttt_status s;
@@ -122,12 +122,14 @@ ttt_status check_acts(const Act &x, int B, int H, int L, int D, int32_t in_dt, i
     if (!x.eta.data) return fail(TTT_ERR_NULL, "eta is NULL");
     if (x.eta.sB < 0 || x.eta.sH < 0) return fail(TTT_ERR_ALIGN, "eta has a negative stride");
     if (!x.ln_w || !x.ln_b) return fail(TTT_ERR_NULL, "ln_w / ln_b is NULL");
+    if (x.eta.token_eta && !aligned16(x.eta.token_eta)) return fail(TTT_ERR_ALIGN, "token_eta must be 16-byte aligned");
     const Range ro = tensor_range(x.out.data, x.out.sB, x.out.sH, x.out.sL, B, H, L, D, eo);
     const Range rin[] = {tensor_range(x.XQ.data, x.XQ.sB, x.XQ.sH, x.XQ.sL, B, H, L, D, ei),
                          tensor_range(x.XK.data, x.XK.sB, x.XK.sH, x.XK.sL, B, H, L, D, ei),
                          tensor_range(x.XV.data, x.XV.sB, x.XV.sH, x.XV.sL, B, H, L, D, ei),
                          tensor_range(x.eta.data, x.eta.sB, x.eta.sH, 1, B, H, L, 1, 4),
-                         flat_range(x.ln_w, (int64_t)H * D, 4), flat_range(x.ln_b, (int64_t)H * D, 4)};
+                         flat_range(x.ln_w, (int64_t)H * D, 4), flat_range(x.ln_b, (int64_t)H * D, 4),
+                         flat_range(x.eta.token_eta, x.eta.token_eta ? K : 0, 4)};
     for (const Range &r : rin)
         if (overlap(ro, r)) return fail(TTT_ERR_ALIAS, "out overlaps an input");
     for (const Range &r : state_ranges)
@@ -191,6 +193,7 @@ LinearArgs linear_args(const ttt_linear_cfg *cfg, const Act &x, ttt_linear_state
     a.eta = x.eta.data;
     a.eta_sB = x.eta.sB;
     a.eta_sH = x.eta.sH;
+    a.te = x.eta.token_eta;
     a.ln_w = x.ln_w;
     a.ln_b = x.ln_b;
     a.W = st->W;
@@ -226,7 +229,7 @@ ttt_status linear_call(Mode mode, const ttt_linear_cfg *cfg, int32_t L, const Ac
         return fail(TTT_ERR_UNSUPPORTED, "unknown grad_layout %d", (int)cfg->grad_layout);
     std::vector<Range> sr;
     if ((s = check_linear_state(cfg, st, sr))) return s;
-    if ((s = check_acts(x, cfg->B, cfg->H, L, cfg->D, cfg->in_dtype, cfg->out_dtype, sr))) return s;
+    if ((s = check_acts(x, cfg->B, cfg->H, L, cfg->D, cfg->K, cfg->in_dtype, cfg->out_dtype, sr))) return s;
 
     const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     const int in_bf16 = cfg->in_dtype == TTT_BF16, out_bf16 = cfg->out_dtype == TTT_BF16;
@@ -358,7 +361,7 @@ ttt_status ttt_mlp_prefill(const ttt_mlp_cfg *cfg, int32_t L, ttt_tensor XQ, ttt
     std::vector<Range> sr;
     if ((s = check_mlp_state(cfg, state, sr, true))) return s;
     const Act x{XQ, XK, XV, out, eta, ln_w, ln_b};
-    if ((s = check_acts(x, cfg->B, cfg->H, L, cfg->D, cfg->in_dtype, cfg->out_dtype, sr))) return s;
+    if ((s = check_acts(x, cfg->B, cfg->H, L, cfg->D, cfg->K, cfg->in_dtype, cfg->out_dtype, sr))) return s;
     if (state->offset % cfg->K != 0)
         return fail(TTT_ERR_UNSUPPORTED, "TTT-MLP prefill needs offset %% K == 0 (offset %lld); continuing an open "
                     "mini-batch is not implemented", (long long)state->offset);
@@ -369,6 +372,7 @@ ttt_status ttt_mlp_prefill(const ttt_mlp_cfg *cfg, int32_t L, ttt_tensor XQ, ttt
     a.eta = eta.data;
     a.eta_sB = eta.sB;
     a.eta_sH = eta.sH;
+    a.te = eta.token_eta;
     a.ln_w = ln_w;
     a.ln_b = ln_b;
     a.W1 = state->W1;

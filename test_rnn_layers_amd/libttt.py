@@ -28,7 +28,7 @@ class ttt_tensor(ctypes.Structure):
 
 
 class ttt_eta(ctypes.Structure):
-    _fields_ = [("data", c_void_p), ("sB", c_int64), ("sH", c_int64)]
+    _fields_ = [("data", c_void_p), ("sB", c_int64), ("sH", c_int64), ("token_eta", c_void_p)]
 
 
 class ttt_linear_cfg(ctypes.Structure):
@@ -111,16 +111,29 @@ def tensor(t) -> ttt_tensor:
     return ttt_tensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
 
 
-def eta_desc(t) -> ttt_eta:
-    """eta as [H, L] (shared over the batch) or [B, H, L], token stride 1."""
+def _check_te(cfg, token_eta):
+    if token_eta is not None and token_eta.numel() != cfg.K:
+        raise ValueError(f"token_eta holds {token_eta.numel()} values; the mini-batch size is {cfg.K}")
+
+
+def eta_desc(t, token_eta=None) -> ttt_eta:
+    """eta as [H, L] (shared over the batch) or [B, H, L], token stride 1;
+    token_eta: None or a contiguous fp32 device tensor of K values."""
     if isinstance(t, ttt_eta):
         return t
     if t.stride(-1) != 1:
         raise ValueError("eta must have token stride 1")
+    te = None
+    if token_eta is not None:
+        import torch
+
+        if token_eta.dim() != 1 or not token_eta.is_contiguous() or token_eta.dtype != torch.float32:
+            raise ValueError("token_eta must be a contiguous fp32 vector of K values")
+        te = token_eta.data_ptr()
     if t.dim() == 2:
-        return ttt_eta(t.data_ptr(), 0, t.stride(0))
+        return ttt_eta(t.data_ptr(), 0, t.stride(0), te)
     if t.dim() == 3:
-        return ttt_eta(t.data_ptr(), t.stride(0), t.stride(1))
+        return ttt_eta(t.data_ptr(), t.stride(0), t.stride(1), te)
     raise ValueError("eta must be [H, L] or [B, H, L]")
 
 
@@ -213,14 +226,18 @@ def _st(state):
     return state.struct if hasattr(state, "struct") else state
 
 
-def ttt_linear_prefill(cfg, L, XQ, XK, XV, eta, ln_w, ln_b, state, out, stream=None):
-    _check(load().ttt_linear_prefill(ctypes.byref(cfg), int(L), tensor(XQ), tensor(XK), tensor(XV), eta_desc(eta),
+def ttt_linear_prefill(cfg, L, XQ, XK, XV, eta, ln_w, ln_b, state, out, stream=None, token_eta=None):
+    _check_te(cfg, token_eta)
+    _check(load().ttt_linear_prefill(ctypes.byref(cfg), int(L), tensor(XQ), tensor(XK), tensor(XV),
+                                     eta_desc(eta, token_eta),
                                      _ptr(ln_w), _ptr(ln_b), ctypes.byref(_st(state)), tensor(out),
                                      _stream(stream)))
 
 
-def ttt_linear_decode(cfg, T, XQ, XK, XV, eta, ln_w, ln_b, state, out, stream=None):
-    _check(load().ttt_linear_decode(ctypes.byref(cfg), int(T), tensor(XQ), tensor(XK), tensor(XV), eta_desc(eta),
+def ttt_linear_decode(cfg, T, XQ, XK, XV, eta, ln_w, ln_b, state, out, stream=None, token_eta=None):
+    _check_te(cfg, token_eta)
+    _check(load().ttt_linear_decode(ctypes.byref(cfg), int(T), tensor(XQ), tensor(XK), tensor(XV),
+                                    eta_desc(eta, token_eta),
                                     _ptr(ln_w), _ptr(ln_b), ctypes.byref(_st(state)), tensor(out),
                                     _stream(stream)))
 
@@ -230,8 +247,10 @@ def ttt_mlp_state_init(cfg, W1, b1, W2, b2, state, stream=None):
                                      ctypes.byref(_st(state)), _stream(stream)))
 
 
-def ttt_mlp_prefill(cfg, L, XQ, XK, XV, eta, ln_w, ln_b, state, out, stream=None):
-    _check(load().ttt_mlp_prefill(ctypes.byref(cfg), int(L), tensor(XQ), tensor(XK), tensor(XV), eta_desc(eta),
+def ttt_mlp_prefill(cfg, L, XQ, XK, XV, eta, ln_w, ln_b, state, out, stream=None, token_eta=None):
+    _check_te(cfg, token_eta)
+    _check(load().ttt_mlp_prefill(ctypes.byref(cfg), int(L), tensor(XQ), tensor(XK), tensor(XV),
+                                  eta_desc(eta, token_eta),
                                   _ptr(ln_w), _ptr(ln_b), ctypes.byref(_st(state)), tensor(out), _stream(stream)))
 
 

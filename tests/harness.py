@@ -25,8 +25,10 @@ class LinearGPU:
     """One TTT-Linear problem on the GPU: device inputs, state, out."""
 
     def __init__(self, inp: dict, *, K=16, rope=False, in_dtype="bf16", out_dtype="f32", layout="bhld",
-                 device="cuda", grad_layout="dense"):
+                 device="cuda", grad_layout="dense", token_eta=None):
         self.inp = inp
+        self.te = None if token_eta is None else torch.tensor(np.asarray(token_eta), dtype=torch.float32,
+                                                              device=device)
         B, H, L, D = inp["XQ"].shape
         self.B, self.H, self.L, self.D = B, H, L, D
         self.grad_layout = grad_layout
@@ -56,7 +58,7 @@ class LinearGPU:
         sl = slice(t0, t1)
         fn = libttt.ttt_linear_decode if decode else libttt.ttt_linear_prefill
         fn(self.cfg, t1 - t0, self.x["XQ"][:, :, sl], self.x["XK"][:, :, sl], self.x["XV"][:, :, sl],
-           self.eta[:, sl], self.ln_w, self.ln_b, self.state, self.out[:, :, sl])
+           self.eta[:, sl], self.ln_w, self.ln_b, self.state, self.out[:, :, sl], token_eta=self.te)
 
     def result(self):
         """out, W, b, and the dense W_grad (built from the open rows in the rows
@@ -71,7 +73,7 @@ class LinearGPU:
         return (to_f64(self.out), to_f64(s.W), to_f64(s.b), G, to_f64(s.b_grad))
 
 
-def oracle_linear(inp: dict, *, K=16, rope=False, chains=None, L=None):
+def oracle_linear(inp: dict, *, K=16, rope=False, chains=None, L=None, token_eta=None):
     """Oracle outputs and final state for the listed (b, h) chains (default all).
     Returns out [n, L, D], W, b, G, gb per chain."""
     B, H, Lf, D = inp["XQ"].shape
@@ -83,7 +85,7 @@ def oracle_linear(inp: dict, *, K=16, rope=False, chains=None, L=None):
     for (b, h) in chains:
         q, k, v = (to_f64(inp[n][b, h, :L]) for n in ("XQ", "XK", "XV"))
         W, bb, G, gb = W0[h].copy(), b0[h].copy(), np.zeros((D, D)), np.zeros(D)
-        o = oracle.linear_chain(q, k, v, eta[h, :L], lw[h], lb[h], W, bb, G, gb, K=K, rope=rope)
+        o = oracle.linear_chain(q, k, v, eta[h, :L], lw[h], lb[h], W, bb, G, gb, K=K, rope=rope, token_eta=token_eta)
         outs.append(o)
         Ws.append(W)
         bs.append(bb)
@@ -95,11 +97,13 @@ def oracle_linear(inp: dict, *, K=16, rope=False, chains=None, L=None):
 class MlpGPU:
     """One TTT-MLP problem on the GPU: device inputs, state, out."""
 
-    def __init__(self, inp: dict, *, K=16, rope=False, out_dtype="f32", device="cuda"):
+    def __init__(self, inp: dict, *, K=16, rope=False, out_dtype="f32", device="cuda", token_eta=None):
         B, H, L, D = inp["XQ"].shape
         F = inp["W1"].shape[-1]
         self.B, self.H, self.L, self.D, self.F = B, H, L, D, F
         self.cfg = libttt.mlp_cfg(B, H, F=F, K=K, in_dtype="bf16", out_dtype=out_dtype, rope=rope)
+        self.te = None if token_eta is None else torch.tensor(np.asarray(token_eta), dtype=torch.float32,
+                                                              device=device)
         self.x = {n: inp[n].to(device).contiguous() for n in ("XQ", "XK", "XV")}
         self.eta = inp["eta"].to(device)
         self.ln_w, self.ln_b = inp["ln_w"].to(device).contiguous(), inp["ln_b"].to(device).contiguous()
@@ -113,14 +117,14 @@ class MlpGPU:
         sl = slice(t0, t1)
         libttt.ttt_mlp_prefill(self.cfg, t1 - t0, self.x["XQ"][:, :, sl], self.x["XK"][:, :, sl],
                                self.x["XV"][:, :, sl], self.eta[:, sl], self.ln_w, self.ln_b, self.state,
-                               self.out[:, :, sl])
+                               self.out[:, :, sl], token_eta=self.te)
 
     def result(self):
         torch.cuda.synchronize()
         return (to_f64(self.out),) + tuple(to_f64(t) for t in self.state.tensors)
 
 
-def oracle_mlp(inp: dict, *, K=16, rope=False, chains=None, L=None):
+def oracle_mlp(inp: dict, *, K=16, rope=False, chains=None, L=None, token_eta=None):
     """Oracle outputs and final state (W1, b1, W2, b2, G1, gb1, G2, gb2) for the
     listed (b, h) chains (default all), each stacked over the chains."""
     B, H, Lf, D = inp["XQ"].shape
@@ -133,7 +137,7 @@ def oracle_mlp(inp: dict, *, K=16, rope=False, chains=None, L=None):
     for (b, h) in chains:
         q, k, v = (to_f64(inp[n][b, h, :L]) for n in ("XQ", "XK", "XV"))
         st = [a[h].copy() for a in init] + [np.zeros((D, F)), np.zeros(F), np.zeros((F, D)), np.zeros(D)]
-        o = oracle.mlp_chain(q, k, v, eta[h, :L], lw[h], lb[h], *st, K=K, rope=rope)
+        o = oracle.mlp_chain(q, k, v, eta[h, :L], lw[h], lb[h], *st, K=K, rope=rope, token_eta=token_eta)
         for i, a in enumerate([o] + st):
             res[i].append(a)
     return tuple(np.stack(r) for r in res)

@@ -95,6 +95,8 @@ CASES = [
     ("eps=0", dict(cfg=_cfg(ln_eps=0.0)), "TTT_ERR_SHAPE"),
     ("dtype", dict(cfg=_cfg(in_dtype=7)), "TTT_ERR_DTYPE"),
     ("grad_layout", dict(cfg=_cfg(grad_layout=2)), "TTT_ERR_UNSUPPORTED"),
+    ("misaligned token_eta", dict(eta=T.ttt_eta(_addr(3), 0, L, _addr(11) + 4)), "TTT_ERR_ALIGN"),
+    ("out overlaps token_eta", dict(eta=T.ttt_eta(_addr(3), 0, L, _addr(10) + 256)), "TTT_ERR_ALIAS"),
     ("misaligned XK", dict(XK=T.ttt_tensor(_addr(1) + 8, H * L * D, L * D, D)), "TTT_ERR_ALIGN"),
     ("odd token stride", dict(XV=T.ttt_tensor(_addr(2), H * L * 68, L * 68, 68 + 2)), "TTT_ERR_ALIGN"),
     ("negative stride", dict(XQ=T.ttt_tensor(_addr(0), H * L * D, L * D, -D)), "TTT_ERR_ALIGN"),

@@ -17,16 +17,17 @@ def _report(name, **kv):
 
 
 def _check_full(name, inp, *, dtype, rope=False, K=16, pieces=None, layout="bhld", out_dtype="f32", decode=(),
-                grad_layout="dense"):
+                grad_layout="dense", token_eta=None):
     """Run the GPU on [0, L) split at `pieces` (list of cut points), compare
     every output and the final state with the oracle."""
     B, H, L, D = inp["XQ"].shape
-    g = LinearGPU(inp, K=K, rope=rope, in_dtype=dtype, out_dtype=out_dtype, layout=layout, grad_layout=grad_layout)
+    g = LinearGPU(inp, K=K, rope=rope, in_dtype=dtype, out_dtype=out_dtype, layout=layout, grad_layout=grad_layout,
+                  token_eta=token_eta)
     cuts = [0] + list(pieces or []) + [L]
     for i in range(len(cuts) - 1):
         g.run(cuts[i], cuts[i + 1], decode=cuts[i] in decode)
     out, W, b, G, gb = g.result()
-    ro, rW, rb, rG, rgb = oracle_linear(inp, K=K, rope=rope)
+    ro, rW, rb, rG, rgb = oracle_linear(inp, K=K, rope=rope, token_eta=token_eta)
     out = out.reshape(B * H, L, D)
     err = max_abs(out, ro)
     tol = tol_for(dtype)
@@ -116,6 +117,58 @@ def test_rows_layout_decode_rope_bf16():
 def test_rows_layout_other_minibatch_sizes(K):
     inp = make_inputs(1, 3, 40, dtype="f32", seed=31 + K, rich=True)
     _check_full(f"rows_K{K}", inp, dtype="f32", K=K, pieces=[7, 20], grad_layout="rows")
+
+
+def _token_eta(K, seed):
+    """1/(i+1) perturbed: distinct values, none equal to 1 past the first."""
+    r = np.random.default_rng(seed)
+    return (1.0 / np.arange(1, K + 1) + 0.05 * r.uniform(size=K)).astype(np.float32).astype(np.float64)
+
+
+# token_eta: the per-position step scale (the pages' third eta factor)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rope", [False, True])
+def test_token_eta_parity(dtype, rope):
+    """Whole mini-batches in the dual kernel and a ragged tail in the token
+    kernel, with a non-constant token_eta."""
+    inp = make_inputs(2, 3, 87, dtype=dtype, seed=61 + rope, rich=True)
+    _check_full(f"token_eta_{dtype}_rope{int(rope)}", inp, dtype=dtype, rope=rope, token_eta=_token_eta(16, 3))
+
+
+@pytest.mark.parametrize("grad_layout", ["dense", "rows"])
+def test_token_eta_pieces_and_decode(grad_layout):
+    """Open mini-batches completed by the token kernel, then single-token
+    decode calls, with token_eta, in both W_grad layouts."""
+    inp = make_inputs(2, 2, 70, dtype="bf16", seed=67, rich=True)
+    cuts = [5, 21, 40] + list(range(41, 70))
+    _check_full(f"token_eta_pieces_{grad_layout}", inp, dtype="bf16", rope=True, pieces=cuts, decode=set(cuts[3:]),
+                grad_layout=grad_layout, token_eta=_token_eta(16, 4))
+
+
+def test_token_eta_other_minibatch_size():
+    inp = make_inputs(1, 3, 40, dtype="f32", seed=71, rich=True)
+    _check_full("token_eta_K13", inp, dtype="f32", K=13, pieces=[7, 20], token_eta=_token_eta(13, 5))
+
+
+def test_constant_token_eta_equals_scaled_eta():
+    """On the GPU: token_eta = c everywhere gives the outputs of token_eta
+    absent with every learning rate times c.  c = 0.5 scales exactly, so on
+    fp32 operands the two agree to rounding (fp16 operands would differ where
+    the halved values fall to fp16 subnormals)."""
+    inp = make_inputs(2, 2, 70, dtype="f32", seed=73, rich=True)
+    a = LinearGPU(inp, in_dtype="f32", token_eta=np.full(16, 0.5))
+    a.run(0, 70)
+    inp2 = dict(inp)
+    inp2["eta"] = inp["eta"] * 0.5
+    b = LinearGPU(inp2, in_dtype="f32")
+    b.run(0, 70)
+    oa, ob = a.result(), b.result()
+    # out, W, b agree; the open mini-batch's accumulated gradients carry the
+    # learning rates but not token_eta, so those of the halved rates are half
+    for x, y in zip(oa[:3], ob[:3]):
+        assert max_abs(x, y) <= 1e-6, max_abs(x, y)
+    for x, y in zip(oa[3:], ob[3:]):
+        assert max_abs(0.5 * x, y) <= 1e-6, max_abs(0.5 * x, y)
 
 
 def test_bf16_output():

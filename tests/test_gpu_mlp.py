@@ -37,15 +37,15 @@ def _compare(name, got, ref, chains, *, out_dtype="f32"):
         assert e <= TOL_BF16, f"{name}: {n} max-abs {e}"
 
 
-def _run(name, inp, *, rope=False, pieces=(), out_dtype="f32", chains=None):
+def _run(name, inp, *, rope=False, pieces=(), out_dtype="f32", chains=None, token_eta=None):
     B, H, L, D = inp["XQ"].shape
-    g = MlpGPU(inp, rope=rope, out_dtype=out_dtype)
+    g = MlpGPU(inp, rope=rope, out_dtype=out_dtype, token_eta=token_eta)
     cuts = [0] + list(pieces) + [L]
     for i in range(len(cuts) - 1):
         g.run(cuts[i], cuts[i + 1])
     got = g.result()
     chains = [(b, h) for b in range(B) for h in range(H)] if chains is None else chains
-    ref = oracle_mlp(inp, rope=rope, chains=chains)
+    ref = oracle_mlp(inp, rope=rope, chains=chains, token_eta=token_eta)
     _compare(name, got, ref, chains, out_dtype=out_dtype)
     assert g.state.offset == L
     return got
@@ -72,6 +72,16 @@ def test_split_calls():
     ends open."""
     inp = make_inputs(2, 2, 117, dtype="bf16", seed=51, rich=True, mlp_hidden=256)
     _run("mlp_split", inp, pieces=(32, 80), rope=True)
+
+
+@pytest.mark.parametrize("L", [87, 96])
+def test_token_eta(L):
+    """A non-constant token_eta (per-position step scale); L = 87 ends in an
+    open mini-batch, whose accumulated gradients carry no token_eta."""
+    r = np.random.default_rng(L)
+    te = (1.0 / np.arange(1, 17) + 0.05 * r.uniform(size=16)).astype(np.float32).astype(np.float64)
+    inp = make_inputs(2, 3, L, dtype="bf16", seed=81 + L, rich=True, mlp_hidden=256)
+    _run(f"mlp_token_eta_L{L}", inp, rope=True, pieces=(32,), token_eta=te)
 
 
 def test_bf16_output():

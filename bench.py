@@ -10,6 +10,8 @@ Other workloads (``--workload``):
   mlp_350m     TTT-MLP prefill, B = 4, H = 16, L = 4096, hidden 256
   decode_1b    B = 64, H = 32: prefill 512 tokens, then 256 single-token
                decode calls; the value is decode tokens/s
+  mlp_decode_350m  TTT-MLP, B = 16, H = 16: prefill 512 tokens, then 64
+               single-token decode calls; the value is decode tokens/s
 
 Prints one JSON line: whole-step throughput, the roofline of the dominant
 kernel (its launches timed with HIP events on the stream they run on), and
@@ -63,6 +65,22 @@ def decode_state_bytes(layout, positions):
     return total / len(positions)
 
 
+def mlp_decode_state_bytes(positions):
+    """Mean state bytes one TTT-MLP chain reads and writes per decode call
+    (dense gradients): W1, b1, W2, b2 read; W1_grad .. b2_grad read unless the
+    mini-batch is empty, and written; W1 .. b2 written by a call that closes
+    the mini-batch."""
+    par = (2 * D * F + F + D) * 4
+    total = 0
+    for pos in positions:
+        p = pos % K
+        n = par + (par if p else 0) + par
+        if p == K - 1:
+            n += par
+        total += n
+    return total / len(positions)
+
+
 # the state a prefill chain reads once and writes once: W, b (fp32)
 LINEAR_STATE_BYTES = 2 * (D * D + D) * 4
 # the state of one TTT-MLP chain, read once and written once: W1, b1, W2, b2
@@ -79,7 +97,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="linear_1b", choices=["linear_1b", "linear_125m", "mlp_350m", "decode_1b"])
+    ap.add_argument("--workload", default="linear_1b",
+                    choices=["linear_1b", "linear_125m", "mlp_350m", "decode_1b", "mlp_decode_350m"])
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--rope", action="store_true", help="rotary on for a linear workload that has it off")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -482,6 +501,108 @@ def bench_decode(args, w):
     return res
 
 
+def cpu_mlp_decode(inp, w, budget):
+    """The oracle's TTT-MLP decode rate: every sequence prefilled over the
+    prefill tokens (untimed), then its decode tokens timed from a copy of that
+    state; only as many batch rows as the budget allows."""
+    import numpy as np
+
+    import oracle
+
+    B, H, P, T = w.B, w.H, w.prefill, w.decode
+    eta, lw, lb = _f64(inp["eta"]), _f64(inp["ln_w"]), _f64(inp["ln_b"])
+    x = {n: _f64(inp[n]) for n in ("XQ", "XK", "XV")}
+    st0 = [_f64(inp[n]) for n in ("W1", "b1", "W2", "b2")]
+    sl = lambda n, r, a, z: np.ascontiguousarray(x[n][r:r + 1, :, a:z])  # noqa: E731
+    rows, dt = 0, 0.0
+    while rows == 0 or dt < budget:
+        r = rows % B
+        st = [np.ascontiguousarray(a[None]) for a in st0]
+        grads = [np.zeros_like(a) for a in st]
+        oracle.mlp_batch(sl("XQ", r, 0, P), sl("XK", r, 0, P), sl("XV", r, 0, P),
+                         np.ascontiguousarray(eta[:, :P]), 0, lw, lb, *st, *grads, K=K)
+        t0 = time.perf_counter()
+        oracle.mlp_batch(sl("XQ", r, P, P + T), sl("XK", r, P, P + T), sl("XV", r, P, P + T),
+                         np.ascontiguousarray(eta[:, P:P + T]), 0, lw, lb, *st, *grads, K=K, offset=P)
+        dt += time.perf_counter() - t0
+        rows += 1
+    return {"value": rows * T / dt, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"{rows} batch rows of the workload's {B}, cycled ({H} heads, {T} decode tokens after a "
+                      f"{P}-token prefill, prefill untimed), fp64 primal form, {dt:.1f} s"}
+
+
+def bench_mlp_decode(args, w):
+    """TTT-MLP: prefill, then single-token decode calls replayed from a HIP
+    graph (as for TTT-Linear decode)."""
+    import torch
+
+    from test_rnn_layers_amd import libttt
+    from test_rnn_layers_amd.synth import workload_inputs
+
+    dev = "cuda"
+    B, H, P, T = w.B, w.H, w.prefill, w.decode
+    inp = workload_inputs(w)
+    cfg = libttt.mlp_cfg(B, H, in_dtype=w.dtype, out_dtype=args.out_dtype)
+    odt = torch.float32 if args.out_dtype == "f32" else torch.bfloat16
+    x = {n: inp[n].to(dev).contiguous() for n in ("XQ", "XK", "XV")}
+    eta = inp["eta"].to(dev).contiguous()
+    lw, lb = inp["ln_w"].to(dev).contiguous(), inp["ln_b"].to(dev).contiguous()
+    init = [inp[n].to(dev).contiguous() for n in ("W1", "b1", "W2", "b2")]
+    out = torch.empty((B, H, P + T, D), dtype=odt, device=dev)
+    st = libttt.MlpState.empty(B, H, D, F, device=dev)
+    views = [tuple(x[n][:, :, t:t + 1] for n in ("XQ", "XK", "XV")) + (eta[:, t:t + 1], out[:, :, t:t + 1])
+             for t in range(P, P + T)]
+
+    def prefill(stream):
+        libttt.ttt_mlp_state_init(cfg, *init, st, stream)
+        libttt.ttt_mlp_prefill(cfg, P, x["XQ"][:, :, :P], x["XK"][:, :, :P], x["XV"][:, :, :P], eta[:, :P],
+                               lw, lb, st, out[:, :, :P], stream)
+
+    def decode_all(stream):
+        for (q, k, v, e, o) in views:
+            libttt.ttt_mlp_decode(cfg, 1, q, k, v, e, lw, lb, st, o, stream)
+
+    cur = torch.cuda.current_stream()
+    prefill(cur)
+    decode_all(cur)
+    prefill(cur)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        decode_all(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    tm = Timer(stream)
+
+    def step(i, timed):
+        prefill(stream)
+        if timed:
+            tm.start("decode")
+        graph.replay()
+        if timed:
+            tm.stop("decode")
+
+    elapsed = run_steps(args, step)
+    dec = stats(tm.ms("decode"))
+    per_tok = linear_token_bytes(w.dtype, args.out_dtype)
+    state_rw = mlp_decode_state_bytes(range(P, P + T))
+    amount = (per_tok + state_rw) * B * H
+    kms = {k: (v / T if k != "n" else v * T) for k, v in dec.items()}
+    res = common(args, w, B * T / (dec["mean"] * 1e-3), elapsed, w.dtype,
+                 {"prefill": P, "decode_steps": T, "mlp_hidden": F,
+                  "decode_launch": f"HIP graph of the {T} decode calls, replayed; per-call time = replay time / {T}",
+                  "decode_phase_ms": dec,
+                  "value_is": f"decode tokens/s over the {T} decode calls (GPU time of the decode phase)"})
+    res["metric"] = f"TTT-MLP decode tokens/sec ({w.name})"
+    res["roofline"] = roofline("mlp_token_kernel", w.name, bound="hbm", amount=amount, kernel_ms=kms,
+                               per_unit=f"{per_tok} B token in/out + {state_rw:g} B state read/write per chain "
+                                        "(dense gradients, mean over the decode positions)",
+                               units=f"{B * H} chains, one token each")
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_mlp_decode(inp, w, args.cpu_seconds)
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -491,8 +612,8 @@ def main():
     from test_rnn_layers_amd.synth import WORKLOADS
 
     w = {"linear_125m": WORKLOADS[1], "linear_1b": WORKLOADS[2], "mlp_350m": WORKLOADS[3],
-         "decode_1b": WORKLOADS[4]}[args.workload]
-    fn = {"linear": bench_linear, "mlp": bench_mlp, "decode": bench_decode}[w.kind]
+         "decode_1b": WORKLOADS[4], "mlp_decode_350m": WORKLOADS[5]}[args.workload]
+    fn = {"linear": bench_linear, "mlp": bench_mlp, "decode": bench_decode, "mlp_decode": bench_mlp_decode}[w.kind]
     res = fn(args, w)
     if args.copy_probe_mb:
         copy_probe(args.copy_probe_mb)

@@ -188,7 +188,7 @@ typedef struct ttt_mlp_cfg {
     int32_t B, H;
     int32_t D;           /* 64 */
     int32_t F;           /* hidden width of the inner MLP, 256 */
-    int32_t K;           /* 16 */
+    int32_t K;           /* mini-batch size 1..16 (16 runs whole mini-batches on MFMA) */
     int32_t in_dtype, out_dtype;
     int32_t rope;
     float rope_base;
@@ -210,14 +210,26 @@ typedef struct ttt_mlp_state {
 ttt_status ttt_mlp_state_init(const ttt_mlp_cfg *cfg, const float *W1, const float *b1, const float *W2,
                               const float *b2, ttt_mlp_state *state, void *stream);
 
-/* TTT-MLP over L tokens in the dual form, whole mini-batches on MFMA.  Needs
- * state->offset % K == 0 (TTT_ERR_UNSUPPORTED otherwise).  A trailing partial
- * mini-batch of r < K tokens is computed with its outputs and left open: the
- * parameters stay at the mini-batch start and the *_grad arrays receive its
- * accumulated eta-weighted gradients.  On success state->offset += L. */
+/* TTT-MLP over L tokens, continuing from the state at any offset (the
+ * TTT-Linear step applied to both layers of the inner MLP: "代码连连看——TTT",
+ * closing remark).  With K = 16 and bf16 inputs, tokens that complete an open
+ * mini-batch run one at a time (primal form), whole mini-batches in the dual
+ * form on MFMA (fp16 operands, fp32 accumulation); a trailing partial
+ * mini-batch is computed with its outputs and left open: the parameters stay
+ * at the mini-batch start and the *_grad arrays hold its accumulated
+ * eta-weighted gradients.  fp32 inputs and K != 16 run every token in the
+ * primal form (fp32 arithmetic).  On success state->offset += L. */
 ttt_status ttt_mlp_prefill(const ttt_mlp_cfg *cfg, int32_t L, ttt_tensor XQ, ttt_tensor XK, ttt_tensor XV,
                            ttt_eta eta, const float *ln_w, const float *ln_b, ttt_mlp_state *state,
                            ttt_tensor out, void *stream);
+
+/* TTT-MLP decode: T tokens (typically 1) one at a time in the primal form
+ * (compute_mini_batch, primal branch, on both layers; fp32 arithmetic); the
+ * step is committed when a token closes a mini-batch.  Same arguments and
+ * errors as ttt_mlp_prefill.  On success state->offset += T. */
+ttt_status ttt_mlp_decode(const ttt_mlp_cfg *cfg, int32_t T, ttt_tensor XQ, ttt_tensor XK, ttt_tensor XV,
+                          ttt_eta eta, const float *ln_w, const float *ln_b, ttt_mlp_state *state,
+                          ttt_tensor out, void *stream);
 
 const char *ttt_status_string(ttt_status s);
 const char *ttt_last_error(void);

@@ -24,12 +24,15 @@ struct MlpArgs {
     int32_t rope;
     float rope_base;
     float eps;
-    const float *te;  // token_eta [16] or nullptr (all ones)
+    const float *te;  // token_eta [K] or nullptr (all ones)
+    int32_t K;        // mini-batch size (token kernel; the dual kernel takes 16)
+    int32_t ntok;     // tokens (token kernel)
 };
 
 hipError_t launch_linear_token(const LinearArgs &a, int in_bf16, int out_bf16, hipStream_t s);
 hipError_t launch_linear_dual(const LinearArgs &a, int in_bf16, int out_bf16, hipStream_t s);
 hipError_t launch_mlp_dual(const MlpArgs &a, int in_bf16, int out_bf16, hipStream_t s);
+hipError_t launch_mlp_token(const MlpArgs &a, int in_bf16, int out_bf16, hipStream_t s);
 hipError_t launch_tile(float *dst, const float *src, int64_t per, int64_t total, hipStream_t s);
 
 }  // namespace ttt

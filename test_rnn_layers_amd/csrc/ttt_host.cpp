@@ -160,9 +160,6 @@ ttt_status check_mlp_cfg(const ttt_mlp_cfg *cfg) {
                           cfg->rope_base, cfg->rope)))
         return s;
     if (cfg->F != 256) return fail(TTT_ERR_SHAPE, "MLP hidden width F=%d unsupported (must be 256)", cfg->F);
-    if (cfg->K != 16) return fail(TTT_ERR_SHAPE, "TTT-MLP needs mini_batch_size 16 (K=%d)", cfg->K);
-    if (cfg->in_dtype != TTT_BF16)
-        return fail(TTT_ERR_UNSUPPORTED, "TTT-MLP takes bf16 inputs (its products run on fp16 operands)");
     return TTT_OK;
 }
 
@@ -276,6 +273,68 @@ ttt_status linear_call(Mode mode, const ttt_linear_cfg *cfg, int32_t L, const Ac
     return ok();
 }
 
+// TTT-MLP call: tokens that complete an open mini-batch run in the token
+// kernel, whole mini-batches (and a trailing partial one) in the dual-form
+// kernel; decode calls, fp32 inputs and K != 16 run token by token.
+ttt_status mlp_call(Mode mode, const ttt_mlp_cfg *cfg, int32_t L, const Act &x, ttt_mlp_state *st,
+                    void *stream) {
+    ttt_status s;
+    if ((s = check_mlp_cfg(cfg))) return s;
+    if (L < 1) return fail(TTT_ERR_SHAPE, "token count %d must be >= 1", L);
+    std::vector<Range> sr;
+    if ((s = check_mlp_state(cfg, st, sr, true))) return s;
+    if ((s = check_acts(x, cfg->B, cfg->H, L, cfg->D, cfg->K, cfg->in_dtype, cfg->out_dtype, sr))) return s;
+    MlpArgs a{};
+    a.q = TDesc{x.XQ.data, x.XQ.sB, x.XQ.sH, x.XQ.sL};
+    a.k = TDesc{x.XK.data, x.XK.sB, x.XK.sH, x.XK.sL};
+    a.v = TDesc{x.XV.data, x.XV.sB, x.XV.sH, x.XV.sL};
+    a.eta = x.eta.data;
+    a.eta_sB = x.eta.sB;
+    a.eta_sH = x.eta.sH;
+    a.te = x.eta.token_eta;
+    a.ln_w = x.ln_w;
+    a.ln_b = x.ln_b;
+    a.W1 = st->W1;
+    a.b1 = st->b1;
+    a.W2 = st->W2;
+    a.b2 = st->b2;
+    a.W1g = st->W1_grad;
+    a.b1g = st->b1_grad;
+    a.W2g = st->W2_grad;
+    a.b2g = st->b2_grad;
+    a.out = ODesc{x.out.data, x.out.sB, x.out.sH, x.out.sL};
+    a.B = cfg->B;
+    a.H = cfg->H;
+    a.K = cfg->K;
+    a.rope = cfg->rope;
+    a.rope_base = cfg->rope_base;
+    a.eps = cfg->ln_eps;
+    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    const int in_bf16 = cfg->in_dtype == TTT_BF16, out_bf16 = cfg->out_dtype == TTT_BF16;
+    const int K = cfg->K;
+    int head = L, rest = 0;  // token kernel for `head` tokens, then the dual kernel for `rest`
+    if (mode == Mode::Prefill && K == 16 && in_bf16) {
+        head = (int)std::min<int64_t>(L, (K - st->offset % K) % K);
+        rest = L - head;
+    }
+    hipError_t e;
+    if (head > 0) {
+        a.ntok = head;
+        a.t0 = 0;
+        a.pos0 = st->offset;
+        if ((e = launch_mlp_token(a, in_bf16, out_bf16, hs)) != hipSuccess) return hip_fail(e, "mlp token kernel");
+    }
+    if (rest > 0) {
+        a.nblk = (rest + K - 1) / K;
+        a.tail = rest % K;
+        a.t0 = head;
+        a.pos0 = st->offset + head;
+        if ((e = launch_mlp_dual(a, in_bf16, out_bf16, hs)) != hipSuccess) return hip_fail(e, "mlp kernel");
+    }
+    st->offset += L;
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -355,49 +414,13 @@ ttt_status ttt_mlp_state_init(const ttt_mlp_cfg *cfg, const float *W1, const flo
 ttt_status ttt_mlp_prefill(const ttt_mlp_cfg *cfg, int32_t L, ttt_tensor XQ, ttt_tensor XK, ttt_tensor XV,
                            ttt_eta eta, const float *ln_w, const float *ln_b, ttt_mlp_state *state, ttt_tensor out,
                            void *stream) {
-    ttt_status s;
-    if ((s = check_mlp_cfg(cfg))) return s;
-    if (L < 1) return fail(TTT_ERR_SHAPE, "token count %d must be >= 1", L);
-    std::vector<Range> sr;
-    if ((s = check_mlp_state(cfg, state, sr, true))) return s;
-    const Act x{XQ, XK, XV, out, eta, ln_w, ln_b};
-    if ((s = check_acts(x, cfg->B, cfg->H, L, cfg->D, cfg->K, cfg->in_dtype, cfg->out_dtype, sr))) return s;
-    if (state->offset % cfg->K != 0)
-        return fail(TTT_ERR_UNSUPPORTED, "TTT-MLP prefill needs offset %% K == 0 (offset %lld); continuing an open "
-                    "mini-batch is not implemented", (long long)state->offset);
-    MlpArgs a{};
-    a.q = TDesc{XQ.data, XQ.sB, XQ.sH, XQ.sL};
-    a.k = TDesc{XK.data, XK.sB, XK.sH, XK.sL};
-    a.v = TDesc{XV.data, XV.sB, XV.sH, XV.sL};
-    a.eta = eta.data;
-    a.eta_sB = eta.sB;
-    a.eta_sH = eta.sH;
-    a.te = eta.token_eta;
-    a.ln_w = ln_w;
-    a.ln_b = ln_b;
-    a.W1 = state->W1;
-    a.b1 = state->b1;
-    a.W2 = state->W2;
-    a.b2 = state->b2;
-    a.W1g = state->W1_grad;
-    a.b1g = state->b1_grad;
-    a.W2g = state->W2_grad;
-    a.b2g = state->b2_grad;
-    a.out = ODesc{out.data, out.sB, out.sH, out.sL};
-    a.B = cfg->B;
-    a.H = cfg->H;
-    a.nblk = (L + cfg->K - 1) / cfg->K;
-    a.tail = L % cfg->K;
-    a.t0 = 0;
-    a.pos0 = state->offset;
-    a.rope = cfg->rope;
-    a.rope_base = cfg->rope_base;
-    a.eps = cfg->ln_eps;
-    hipError_t e = launch_mlp_dual(a, cfg->in_dtype == TTT_BF16, cfg->out_dtype == TTT_BF16,
-                                   reinterpret_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "mlp kernel");
-    state->offset += L;
-    return ok();
+    return mlp_call(Mode::Prefill, cfg, L, Act{XQ, XK, XV, out, eta, ln_w, ln_b}, state, stream);
+}
+
+ttt_status ttt_mlp_decode(const ttt_mlp_cfg *cfg, int32_t T, ttt_tensor XQ, ttt_tensor XK, ttt_tensor XV,
+                          ttt_eta eta, const float *ln_w, const float *ln_b, ttt_mlp_state *state, ttt_tensor out,
+                          void *stream) {
+    return mlp_call(Mode::Decode, cfg, T, Act{XQ, XK, XV, out, eta, ln_w, ln_b}, state, stream);
 }
 
 }  // extern "C"

@@ -20,7 +20,7 @@ TTT_F32, TTT_BF16 = 0, 1
 TTT_GRAD_DENSE, TTT_GRAD_ROWS = 0, 1
 
 EXPORTS = ["ttt_linear_state_init", "ttt_linear_prefill", "ttt_linear_decode", "ttt_mlp_state_init",
-           "ttt_mlp_prefill", "ttt_status_string", "ttt_last_error"]
+           "ttt_mlp_prefill", "ttt_mlp_decode", "ttt_status_string", "ttt_last_error"]
 
 
 class ttt_tensor(ctypes.Structure):
@@ -84,8 +84,9 @@ def load():
                                        c_void_p]
     lib.ttt_mlp_prefill.argtypes = [P(ttt_mlp_cfg), c_int32, ttt_tensor, ttt_tensor, ttt_tensor, ttt_eta, c_void_p,
                                     c_void_p, P(ttt_mlp_state), ttt_tensor, c_void_p]
+    lib.ttt_mlp_decode.argtypes = lib.ttt_mlp_prefill.argtypes
     for f in ("ttt_linear_state_init", "ttt_linear_prefill", "ttt_linear_decode", "ttt_mlp_state_init",
-              "ttt_mlp_prefill"):
+              "ttt_mlp_prefill", "ttt_mlp_decode"):
         getattr(lib, f).restype = c_int32
     _lib = lib
     return lib
@@ -252,6 +253,13 @@ def ttt_mlp_prefill(cfg, L, XQ, XK, XV, eta, ln_w, ln_b, state, out, stream=None
     _check(load().ttt_mlp_prefill(ctypes.byref(cfg), int(L), tensor(XQ), tensor(XK), tensor(XV),
                                   eta_desc(eta, token_eta),
                                   _ptr(ln_w), _ptr(ln_b), ctypes.byref(_st(state)), tensor(out), _stream(stream)))
+
+
+def ttt_mlp_decode(cfg, T, XQ, XK, XV, eta, ln_w, ln_b, state, out, stream=None, token_eta=None):
+    _check_te(cfg, token_eta)
+    _check(load().ttt_mlp_decode(ctypes.byref(cfg), int(T), tensor(XQ), tensor(XK), tensor(XV),
+                                 eta_desc(eta, token_eta),
+                                 _ptr(ln_w), _ptr(ln_b), ctypes.byref(_st(state)), tensor(out), _stream(stream)))
 
 
 def ttt_status_string(status: int) -> str:

@@ -27,14 +27,14 @@ import statistics
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 KERNEL_SOURCES = {"linear_dual_kernel": "linear_dual.hip", "mlp_dual_kernel": "mlp_dual.hip",
-                  "linear_token_kernel": "linear_token.hip"}
+                  "linear_token_kernel": "linear_token.hip", "mlp_token_kernel": "mlp_token.hip"}
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def source_digest(kernel: str) -> str:
     """sha256 over the kernel's source file and the headers it includes."""
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[kernel], "device_common.hpp", "launch.hpp"):
+    for f in (KERNEL_SOURCES[kernel], "device_common.hpp", "launch.hpp", "gelu.hpp"):
         with open(os.path.join(PKG, "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()

@@ -30,7 +30,7 @@ MLP_HIDDEN = 256
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str          # "linear", "mlp" or "decode"
+    kind: str          # "linear", "mlp", "decode" (TTT-Linear) or "mlp_decode"
     B: int
     H: int
     L: int
@@ -48,6 +48,8 @@ WORKLOADS = [
     Workload("mlp_350m_B4_H16_L4096_F256_bf16", "mlp", 4, 16, 4096, "bf16", False, 1237),
     Workload("decode_1b_B64_H32_prefill512_decode256_bf16", "decode", 64, 32, 768, "bf16", False, 1238,
              prefill=512, decode=256),
+    Workload("mlp_decode_350m_B16_H16_prefill512_decode64_bf16", "mlp_decode", 16, 16, 576, "bf16", False, 1239,
+             prefill=512, decode=64),
 ]
 
 
@@ -91,4 +93,4 @@ def make_inputs(B: int, H: int, L: int, *, D: int = D_HEAD, dtype: str = "f32", 
 
 def workload_inputs(w: Workload) -> dict:
     return make_inputs(w.B, w.H, w.L, dtype=w.dtype, seed=w.seed,
-                       mlp_hidden=MLP_HIDDEN if w.kind == "mlp" else 0)
+                       mlp_hidden=MLP_HIDDEN if w.kind in ("mlp", "mlp_decode") else 0)

@@ -97,11 +97,12 @@ def oracle_linear(inp: dict, *, K=16, rope=False, chains=None, L=None, token_eta
 class MlpGPU:
     """One TTT-MLP problem on the GPU: device inputs, state, out."""
 
-    def __init__(self, inp: dict, *, K=16, rope=False, out_dtype="f32", device="cuda", token_eta=None):
+    def __init__(self, inp: dict, *, K=16, rope=False, out_dtype="f32", device="cuda", token_eta=None,
+                 in_dtype="bf16"):
         B, H, L, D = inp["XQ"].shape
         F = inp["W1"].shape[-1]
         self.B, self.H, self.L, self.D, self.F = B, H, L, D, F
-        self.cfg = libttt.mlp_cfg(B, H, F=F, K=K, in_dtype="bf16", out_dtype=out_dtype, rope=rope)
+        self.cfg = libttt.mlp_cfg(B, H, F=F, K=K, in_dtype=in_dtype, out_dtype=out_dtype, rope=rope)
         self.te = None if token_eta is None else torch.tensor(np.asarray(token_eta), dtype=torch.float32,
                                                               device=device)
         self.x = {n: inp[n].to(device).contiguous() for n in ("XQ", "XK", "XV")}
@@ -113,9 +114,10 @@ class MlpGPU:
         w = [inp[n].to(device).contiguous() for n in ("W1", "b1", "W2", "b2")]
         libttt.ttt_mlp_state_init(self.cfg, *w, self.state)
 
-    def run(self, t0, t1):
+    def run(self, t0, t1, decode=False):
         sl = slice(t0, t1)
-        libttt.ttt_mlp_prefill(self.cfg, t1 - t0, self.x["XQ"][:, :, sl], self.x["XK"][:, :, sl],
+        fn = libttt.ttt_mlp_decode if decode else libttt.ttt_mlp_prefill
+        fn(self.cfg, t1 - t0, self.x["XQ"][:, :, sl], self.x["XK"][:, :, sl],
                                self.x["XV"][:, :, sl], self.eta[:, sl], self.ln_w, self.ln_b, self.state,
                                self.out[:, :, sl], token_eta=self.te)
 

@@ -152,7 +152,7 @@ def _mlp_state(offset=0, **over):
     return T.ttt_mlp_state(*p, offset)
 
 
-def _mlp_call(**over):
+def _mlp_call(fn="ttt_mlp_prefill", **over):
     a = dict(cfg=_mlp_cfg(), L=L, XQ=T.ttt_tensor(_addr(0), H * L * D, L * D, D),
              XK=T.ttt_tensor(_addr(1), H * L * D, L * D, D), XV=T.ttt_tensor(_addr(2), H * L * D, L * D, D),
              eta=T.ttt_eta(_addr(3), 0, L), ln_w=_addr(4), ln_b=_addr(5), state=_mlp_state(),
@@ -160,8 +160,8 @@ def _mlp_call(**over):
     a.update(over)
     cfg = ctypes.byref(a["cfg"]) if a["cfg"] is not None else None
     st = ctypes.byref(a["state"]) if a["state"] is not None else None
-    rc = T.load().ttt_mlp_prefill(cfg, a["L"], a["XQ"], a["XK"], a["XV"], a["eta"], a["ln_w"], a["ln_b"], st,
-                                  a["out"], None)
+    rc = getattr(T.load(), fn)(cfg, a["L"], a["XQ"], a["XK"], a["XV"], a["eta"], a["ln_w"], a["ln_b"], st,
+                               a["out"], None)
     return rc, a
 
 
@@ -171,11 +171,12 @@ MLP_CASES = [
     ("null W2_grad", dict(state=_mlp_state(s6=None)), "TTT_ERR_NULL"),
     ("null XV", dict(XV=T.ttt_tensor(None, H * L * D, L * D, D)), "TTT_ERR_NULL"),
     ("F=128", dict(cfg=_mlp_cfg(F=128)), "TTT_ERR_SHAPE"),
-    ("K=8", dict(cfg=_mlp_cfg(K=8)), "TTT_ERR_SHAPE"),
+    ("K=0", dict(cfg=_mlp_cfg(K=0)), "TTT_ERR_SHAPE"),
+    ("K=17", dict(cfg=_mlp_cfg(K=17)), "TTT_ERR_SHAPE"),
     ("D=32", dict(cfg=_mlp_cfg(D=32)), "TTT_ERR_SHAPE"),
     ("L=0", dict(L=0), "TTT_ERR_SHAPE"),
-    ("fp32 inputs", dict(cfg=_mlp_cfg(in_dtype=T.TTT_F32)), "TTT_ERR_UNSUPPORTED"),
-    ("open mini-batch offset", dict(state=_mlp_state(offset=5)), "TTT_ERR_UNSUPPORTED"),
+    ("dtype", dict(cfg=_mlp_cfg(in_dtype=7)), "TTT_ERR_DTYPE"),
+    ("misaligned token_eta", dict(eta=T.ttt_eta(_addr(3), 0, L, _addr(11) + 8)), "TTT_ERR_ALIGN"),
     ("negative offset", dict(state=_mlp_state(offset=-16)), "TTT_ERR_STATE"),
     ("misaligned b1", dict(state=_mlp_state(s1=_addr(21) + 4)), "TTT_ERR_ALIGN"),
     ("state buffers overlap", dict(state=_mlp_state(s3=_addr(20) + 1024)), "TTT_ERR_ALIAS"),
@@ -184,9 +185,10 @@ MLP_CASES = [
 ]
 
 
+@pytest.mark.parametrize("fn", ["ttt_mlp_prefill", "ttt_mlp_decode"])
 @pytest.mark.parametrize("label,over,expect", MLP_CASES, ids=[c[0] for c in MLP_CASES])
-def test_mlp_error_paths(label, over, expect):
-    rc, a = _mlp_call(**over)
+def test_mlp_error_paths(fn, label, over, expect):
+    rc, a = _mlp_call(fn, **over)
     assert T.STATUS_NAMES[rc] == expect, (label, T.ttt_last_error())
     assert T.ttt_last_error()
     if a["state"] is not None:

@@ -19,7 +19,7 @@ def _report(name, **kv):
           flush=True)
 
 
-def _compare(name, got, ref, chains, *, out_dtype="f32"):
+def _compare(name, got, ref, chains, *, out_dtype="f32", tol=TOL_BF16):
     """got: GPU (out, 8 state arrays) over all chains; ref: oracle over `chains`."""
     B, H = got[0].shape[:2]
     idx = [b * H + h for (b, h) in chains]
@@ -30,23 +30,24 @@ def _compare(name, got, ref, chains, *, out_dtype="f32"):
     _report(name, out=err, **errs)
     assert np.isfinite(out).all()
     if out_dtype == "bf16":
-        assert np.max(np.abs(out - ro) - bf16_half_ulp(ro)) <= TOL_BF16
+        assert np.max(np.abs(out - ro) - bf16_half_ulp(ro)) <= tol
     else:
-        assert err <= TOL_BF16, f"{name}: output max-abs {err}"
+        assert err <= tol, f"{name}: output max-abs {err}"
     for n, e in errs.items():
-        assert e <= TOL_BF16, f"{name}: {n} max-abs {e}"
+        assert e <= tol, f"{name}: {n} max-abs {e}"
 
 
-def _run(name, inp, *, rope=False, pieces=(), out_dtype="f32", chains=None, token_eta=None):
+def _run(name, inp, *, rope=False, pieces=(), out_dtype="f32", chains=None, token_eta=None, K=16, in_dtype="bf16",
+         decode=(), tol=TOL_BF16):
     B, H, L, D = inp["XQ"].shape
-    g = MlpGPU(inp, rope=rope, out_dtype=out_dtype, token_eta=token_eta)
+    g = MlpGPU(inp, rope=rope, out_dtype=out_dtype, token_eta=token_eta, K=K, in_dtype=in_dtype)
     cuts = [0] + list(pieces) + [L]
     for i in range(len(cuts) - 1):
-        g.run(cuts[i], cuts[i + 1])
+        g.run(cuts[i], cuts[i + 1], decode=cuts[i] in decode)
     got = g.result()
     chains = [(b, h) for b in range(B) for h in range(H)] if chains is None else chains
-    ref = oracle_mlp(inp, rope=rope, chains=chains, token_eta=token_eta)
-    _compare(name, got, ref, chains, out_dtype=out_dtype)
+    ref = oracle_mlp(inp, rope=rope, chains=chains, token_eta=token_eta, K=K)
+    _compare(name, got, ref, chains, out_dtype=out_dtype, tol=tol)
     assert g.state.offset == L
     return got
 
@@ -84,6 +85,57 @@ def test_token_eta(L):
     _run(f"mlp_token_eta_L{L}", inp, rope=True, pieces=(32,), token_eta=te)
 
 
+# --- the primal (token) path: decoding, open mini-batches, fp32 inputs, K != 16
+def test_decode_steps():
+    """Prefill 20 tokens (ends inside a mini-batch), then single-token decode
+    calls across two mini-batch boundaries, with rotary."""
+    inp = make_inputs(2, 2, 52, dtype="bf16", seed=91, rich=True, mlp_hidden=256)
+    cuts = [20] + list(range(21, 52))
+    _run("mlp_decode", inp, rope=True, pieces=cuts, decode=set(cuts))
+
+
+def test_prefill_from_open_minibatches():
+    """Prefill calls that start inside a mini-batch: the head runs in the
+    token kernel, the rest in the dual kernel."""
+    inp = make_inputs(2, 3, 90, dtype="bf16", seed=92, rich=True, mlp_hidden=256)
+    _run("mlp_open_pieces", inp, pieces=(5, 21, 40, 41, 75))
+
+
+def test_fp32_inputs():
+    """fp32 inputs run token by token in fp32 arithmetic: 1e-4 bar."""
+    inp = make_inputs(1, 3, 37, dtype="f32", seed=93, rich=True, mlp_hidden=256)
+    _run("mlp_f32", inp, in_dtype="f32", pieces=(10,), tol=1e-4)
+
+
+@pytest.mark.parametrize("K", [1, 8])
+def test_other_minibatch_sizes(K):
+    inp = make_inputs(1, 2, 30, dtype="f32", seed=94 + K, rich=True, mlp_hidden=256)
+    _run(f"mlp_K{K}", inp, in_dtype="f32", K=K, pieces=(7, 13), tol=1e-4)
+
+
+def test_decode_token_eta():
+    r = np.random.default_rng(5)
+    te = (1.0 / np.arange(1, 17) + 0.05 * r.uniform(size=16)).astype(np.float32).astype(np.float64)
+    inp = make_inputs(1, 3, 40, dtype="bf16", seed=95, rich=True, mlp_hidden=256)
+    cuts = [9] + list(range(10, 40))
+    _run("mlp_decode_token_eta", inp, pieces=cuts, decode=set(cuts), token_eta=te)
+
+
+def test_decode_matches_prefill():
+    """The same tokens prefilled in one call (dual kernel) and decoded one at
+    a time (token kernel): outputs and state agree to the fp16-operand bar."""
+    inp = make_inputs(2, 2, 48, dtype="bf16", seed=96, rich=True, mlp_hidden=256)
+    a = MlpGPU(inp)
+    a.run(0, 48)
+    b = MlpGPU(inp)
+    b.run(0, 16)
+    for t in range(16, 48):
+        b.run(t, t + 1, decode=True)
+    ra, rb = a.result(), b.result()
+    for x, y in zip(ra, rb):
+        assert max_abs(x, y) <= TOL_BF16, max_abs(x, y)
+
+
 def test_bf16_output():
     inp = make_inputs(1, 3, 70, dtype="bf16", seed=52, rich=True, mlp_hidden=256)
     _run("mlp_bf16_out", inp, out_dtype="bf16")
@@ -112,14 +164,11 @@ def test_determinism():
         assert np.array_equal(x, y)
 
 
-def test_open_offset_is_refused():
-    """A call may only start on a mini-batch boundary."""
+def test_open_offset_continues():
+    """A call that starts inside a mini-batch continues it (it used to be
+    refused): 20 tokens, then 20 more, equal to the oracle over all 40."""
     inp = make_inputs(1, 1, 40, dtype="bf16", seed=55, mlp_hidden=256)
-    g = MlpGPU(inp)
-    g.run(0, 20)
-    with pytest.raises(libttt.TTTError) as e:
-        g.run(20, 40)
-    assert e.value.name == "TTT_ERR_UNSUPPORTED"
+    _run("mlp_open_continue", inp, pieces=(20,))
 
 
 def test_full_350m_workload_sampled():
@@ -129,3 +178,15 @@ def test_full_350m_workload_sampled():
     inp = workload_inputs(w)
     B, H = w.B, w.H
     _run(w.name, inp, chains=[(0, 0), (1, 7), (2, 11), (B - 1, H - 1)])
+
+
+def test_decode_workload_sampled():
+    """The TTT-MLP decode workload (B16 H16: prefill 512 tokens in the dual
+    kernel, then 64 single-token decode calls in the token kernel); the oracle
+    checks sampled chains."""
+    w = next(x for x in WORKLOADS if x.kind == "mlp_decode")
+    inp = workload_inputs(w)
+    B, H, L = w.B, w.H, w.L
+    cuts = [w.prefill] + list(range(w.prefill + 1, L))
+    _run(w.name, inp, pieces=cuts, decode=set(cuts), chains=[(0, 0), (7, 5), (B - 1, H - 1)])
+

@@ -14,14 +14,21 @@
 // with t_p the token_eta of the token's position p in its mini-batch; at the
 // end of a mini-batch W -= t_p G, b -= t_p gb and the gradients are cleared.
 //
-// One workgroup of 256 threads per (batch, head) chain; thread f owns hidden
-// unit f: column f of W1 and G1 stays in registers for the whole call, row f
-// of W2 and G2 is read from memory when needed.  The 64-wide sums over the
-// hidden units (x2 W2, xb2 W2) are split over the four waves (64 units each,
-// lane = output column) and added by wave 0, which also runs both LayerNorms.
-// The prediction needs the G2 of all units after this token's update; it is
-// formed from the G2 before the update plus the rank-one term
-// eta (xb2 . x2) g2, so no thread reads a G2 row another thread is writing.
+// One workgroup of 512 threads (8 waves) per (batch, head) chain; the whole
+// state stays in registers for the call, 128 values per thread:
+//  * unit waves 0..3: thread f = 64w + c holds column f of W1 and G1; they
+//    form z1, GELU(z1), GELU'(z1), the G1 step and zb1 = q (W1 - t G1) + ...
+//    as in-thread chains over the token's k or q (LDS broadcasts);
+//  * block waves 4..7: lane c of wave 4 + v holds the block
+//    W2[64v .. 64v+63][c] and the same block of G2; they form the sums over
+//    their 64 units of x2 W2 and xb2 (W2 - t G2) for column c (added over the
+//    four block waves by wave 0), the G2 step, and g2 W2^T: each lane writes
+//    its 64 products to a per-wave LDS tile and reads back one row (one
+//    wave's LDS accesses execute in order, so no barrier in between);
+//  * wave 0 also loads the token and runs both LayerNorms.
+// The two roles keep their state in the same two register arrays.  A call
+// reads and writes the state once; per token it reads q, k, v, eta and
+// writes one output row.
 #include "device_common.hpp"
 #include "gelu.hpp"
 #include "launch.hpp"
@@ -32,17 +39,20 @@ namespace {
 constexpr int kF = 256;
 
 template <typename Tin, typename Tout>
-__global__ __launch_bounds__(256, 1) void mlp_token_kernel(MlpArgs a) {
+__global__ __launch_bounds__(512, 1) void mlp_token_kernel(MlpArgs a) {
     const int ch = blockIdx.x;
     const int bi = ch / a.H, hi = ch % a.H;
-    const int f = threadIdx.x;          // hidden unit
-    const int w = f >> 6, c = f & 63;   // wave; lane = output column in the sums over units
+    const int w = threadIdx.x >> 6, c = threadIdx.x & 63;
+    const bool unit_wave = w < 4;
+    const int f = threadIdx.x;        // unit waves: hidden unit of the W1 column
+    const int v = w - 4;              // block waves: units 64v .. 64v+63, column c
 
     __shared__ __align__(16) float sq[kD], sk[kD];
     __shared__ __align__(16) float x2s[kF], xb2s[kF];
-    __shared__ __align__(16) float g2s[kD];
+    __shared__ float dws[kF];          // (g2 W2^T)[u]
+    __shared__ float g2s[kD];
     __shared__ float part[4][kD];
-    __shared__ float red[4];
+    __shared__ float tr[4][kD / 2][kD + 1];  // per block wave: products W2[64v + j][c] g2[c] at [j mod 32][c]
     __shared__ float rcs[16][kD], rsn[16][kD];
 
     const int64_t cD = (int64_t)ch * kD;
@@ -59,19 +69,32 @@ __global__ __launch_bounds__(256, 1) void mlp_token_kernel(MlpArgs a) {
     const float *ep = a.eta + bi * a.eta_sB + hi * a.eta_sH;
     Tout *op = (Tout *)a.out.p + bi * a.out.sB + hi * a.out.sH;
 
-    // state of unit f
-    float W1r[kD], G1r[kD];
+    // the state: unit waves S = W1[:, f], T = G1[:, f]; block waves
+    // S = W2[64v + j][c], T = G2[64v + j][c]
+    float S[kD], T[kD];
+    const int64_t blk = (int64_t)(64 * v) * kD + c;  // block waves: offset of W2[64v][c]
+    if (unit_wave) {
 #pragma unroll
-    for (int i = 0; i < kD; ++i) W1r[i] = W1c[i * kF + f];
-    if (g_clear) {
-#pragma unroll
-        for (int i = 0; i < kD; ++i) G1r[i] = 0.f;
+        for (int j = 0; j < kD; ++j) S[j] = W1c[j * kF + f];
     } else {
 #pragma unroll
-        for (int i = 0; i < kD; ++i) G1r[i] = G1c[i * kF + f];
+        for (int j = 0; j < kD; ++j) S[j] = W2c[blk + j * kD];
     }
-    float b1 = a.b1[(int64_t)ch * kF + f];
-    float gb1 = g_clear ? 0.f : a.b1g[(int64_t)ch * kF + f];
+    if (g_clear) {
+#pragma unroll
+        for (int j = 0; j < kD; ++j) T[j] = 0.f;
+    } else if (unit_wave) {
+#pragma unroll
+        for (int j = 0; j < kD; ++j) T[j] = G1c[j * kF + f];
+    } else {
+#pragma unroll
+        for (int j = 0; j < kD; ++j) T[j] = G2c[blk + j * kD];
+    }
+    float b1 = 0.f, gb1 = 0.f;
+    if (unit_wave) {
+        b1 = a.b1[(int64_t)ch * kF + f];
+        gb1 = g_clear ? 0.f : a.b1g[(int64_t)ch * kF + f];
+    }
     // wave 0: column c of b2, gb2 and of the LayerNorm parameters
     float b2 = 0.f, gb2 = 0.f, gam = 0.f, bet = 0.f;
     if (w == 0) {
@@ -101,9 +124,6 @@ __global__ __launch_bounds__(256, 1) void mlp_token_kernel(MlpArgs a) {
         const int p = (int)((a.pos0 + t) % K);
         const float e = ep[tok];
         const float tp = lane_value(te_c, p);  // the same in every wave
-        // the first token of a mini-batch finds G2 cleared (by the commit
-        // before it, or at a call that starts on a boundary): not read
-        const bool g2_zero = p == 0;
         float qv = 0.f, kv = 0.f, vv = 0.f;
         if (w == 0) {
             qv = to_f32(qp[(int64_t)tok * a.q.sL + c]);
@@ -121,31 +141,36 @@ __global__ __launch_bounds__(256, 1) void mlp_token_kernel(MlpArgs a) {
         }
         __syncthreads();
 
-        // z1 = k W1 + b1 at the block-start state; GELU and GELU'
-        float z4[4] = {b1, 0.f, 0.f, 0.f};
+        // unit waves: z1 = k W1 + b1 at the block-start state; GELU, GELU'
+        float dg = 0.f;
+        if (unit_wave) {
+            float z4[4] = {b1, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < kD; i += 4) {
-            const f32x4 k4 = *(const f32x4 *)&sk[i];
+            for (int i = 0; i < kD; i += 4) {
+                const f32x4 k4 = *(const f32x4 *)&sk[i];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) z4[j] = fmaf(k4[j], W1r[i + j], z4[j]);
+                for (int j = 0; j < 4; ++j) z4[j] = fmaf(k4[j], S[i + j], z4[j]);
+            }
+            const Gelu gz = gelu_both((z4[0] + z4[1]) + (z4[2] + z4[3]));
+            x2s[f] = gz.g;
+            dg = gz.dg;
         }
-        const Gelu gz = gelu_both((z4[0] + z4[1]) + (z4[2] + z4[3]));
-        const float x2 = gz.g;
-        x2s[f] = x2;
         __syncthreads();
 
-        // z2 = x2 W2 + b2: wave w sums units 64w .. 64w+63 for column c
-        {
-            const float *w2 = W2c + (int64_t)(64 * w) * kD + c;
+        // block waves: their units' part of z2 = x2 W2 for column c
+        if (!unit_wave) {
             float s4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 16
-            for (int j = 0; j < 64; ++j) s4[j & 3] = fmaf(x2s[64 * w + j], w2[j * kD], s4[j & 3]);
-            part[w][c] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+#pragma unroll
+            for (int j = 0; j < kD; j += 4) {
+                const f32x4 x4 = *(const f32x4 *)&x2s[64 * v + j];
+#pragma unroll
+                for (int l = 0; l < 4; ++l) s4[l] = fmaf(x4[l], S[j + l], s4[l]);
+            }
+            part[v][c] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
         }
         __syncthreads();
 
         // wave 0: the LayerNorm backward of the reconstruction loss -> g2
-        float g2 = 0.f;
         if (w == 0) {
             const float z = ((part[0][c] + part[1][c]) + (part[2][c] + part[3][c])) + b2;
             float s1 = z, s2 = z * z;
@@ -159,71 +184,79 @@ __global__ __launch_bounds__(256, 1) void mlp_token_kernel(MlpArgs a) {
             wave_sum2(su, sux);
             su *= (1.f / kD);
             sux *= (1.f / kD);
-            g2 = (u - su - xh * sux) * rs;
-            g2s[c] = g2;
+            g2s[c] = (u - su - xh * sux) * rs;
         }
         __syncthreads();
 
-        // unit f: g1 = (W2[f, :] . g2) GELU'(z1); accumulate the gradients of W1, b1
-        float dw = 0.f;
-        {
-            const f32x4 *w2r = (const f32x4 *)(W2c + (int64_t)f * kD);
-            float d4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-            for (int m = 0; m < kD / 4; ++m) {
-                const f32x4 wv = w2r[m];
-                const f32x4 gv = *(const f32x4 *)&g2s[4 * m];
+        const float g2c = g2s[c];
+        if (!unit_wave) {
+            // g2 W2^T for unit 64v + c: row c of this wave's product tile, in
+            // two halves of 32 units.  The reads take values other lanes wrote:
+            // they rely on the wave's LDS accesses executing in program order,
+            // so the compiler must not move them across the writes (for one
+            // lane it can prove the addresses distinct): a memory clobber
+            // between the two.
 #pragma unroll
-                for (int j = 0; j < 4; ++j) d4[j] = fmaf(wv[j], gv[j], d4[j]);
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int j = 0; j < kD / 2; ++j) tr[v][j][c] = S[32 * h + j] * g2c;
+                asm volatile("" ::: "memory");
+                if ((c >> 5) == h) {
+                    float d4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int k = 0; k < kD; ++k) d4[k & 3] += tr[v][c & 31][k];
+                    dws[64 * v + c] = (d4[0] + d4[1]) + (d4[2] + d4[3]);
+                }
+                asm volatile("" ::: "memory");
             }
-            dw = (d4[0] + d4[1]) + (d4[2] + d4[3]);
-        }
-        const float eg1 = e * (dw * gz.dg);
-        gb1 += eg1;
-        // prediction of the first layer with W1 - t_p G1, b1 - t_p gb1
-        float zb4[4] = {fmaf(-tp, gb1, b1), 0.f, 0.f, 0.f};
+            // the G2 step of the block: G2[u][c] += eta x2[u] g2[c]
+            const float eg2c = e * g2c;
 #pragma unroll
-        for (int i = 0; i < kD; i += 4) {
-            const f32x4 k4 = *(const f32x4 *)&sk[i];
-            const f32x4 q4 = *(const f32x4 *)&sq[i];
+            for (int j = 0; j < kD; j += 4) {
+                const f32x4 x4 = *(const f32x4 *)&x2s[64 * v + j];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                G1r[i + j] = fmaf(k4[j], eg1, G1r[i + j]);
-                zb4[j] = fmaf(q4[j], fmaf(-tp, G1r[i + j], W1r[i + j]), zb4[j]);
+                for (int l = 0; l < 4; ++l) T[j + l] = fmaf(x4[l], eg2c, T[j + l]);
             }
         }
-        const float xb2 = gelu((zb4[0] + zb4[1]) + (zb4[2] + zb4[3]));
-        xb2s[f] = xb2;
-        // xb2 . x2 over the units, for the rank-one part of this token's G2 step
-        float dot = xb2 * x2, dummy = 0.f;
-        wave_sum2(dot, dummy);
-        if (c == 0) red[w] = dot;
         __syncthreads();
 
-        // zb2 partial sums with the G2 before this token's step
-        {
-            const float *w2 = W2c + (int64_t)(64 * w) * kD + c;
-            const float *g2p = G2c + (int64_t)(64 * w) * kD + c;
+        // unit waves: g1 = (g2 W2^T) GELU'(z1); the G1 step; the prediction of
+        // the first layer with W1 - t_p G1, b1 - t_p gb1
+        if (unit_wave) {
+            const float eg1 = e * (dws[f] * dg);
+            gb1 += eg1;
+            float zb4[4] = {fmaf(-tp, gb1, b1), 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < kD; i += 4) {
+                const f32x4 k4 = *(const f32x4 *)&sk[i];
+                const f32x4 q4 = *(const f32x4 *)&sq[i];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    T[i + j] = fmaf(k4[j], eg1, T[i + j]);
+                    zb4[j] = fmaf(q4[j], fmaf(-tp, T[i + j], S[i + j]), zb4[j]);
+                }
+            }
+            xb2s[f] = gelu((zb4[0] + zb4[1]) + (zb4[2] + zb4[3]));
+        }
+        __syncthreads();
+
+        // block waves: zb2 = xb2 (W2 - t_p G2) over their units for column c
+        if (!unit_wave) {
             float s4[4] = {0.f, 0.f, 0.f, 0.f};
-            if (g2_zero) {
-#pragma unroll 16
-                for (int j = 0; j < 64; ++j) s4[j & 3] = fmaf(xb2s[64 * w + j], w2[j * kD], s4[j & 3]);
-            } else {
-#pragma unroll 8
-                for (int j = 0; j < 64; ++j)
-                    s4[j & 3] = fmaf(xb2s[64 * w + j], fmaf(-tp, g2p[j * kD], w2[j * kD]), s4[j & 3]);
+#pragma unroll
+            for (int j = 0; j < kD; j += 4) {
+                const f32x4 x4 = *(const f32x4 *)&xb2s[64 * v + j];
+#pragma unroll
+                for (int l = 0; l < 4; ++l) s4[l] = fmaf(x4[l], fmaf(-tp, T[j + l], S[j + l]), s4[l]);
             }
-            part[w][c] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+            part[v][c] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
         }
         __syncthreads();
 
-        // wave 0: zb2 = xb2 (W2 - t_p G2) + b2 - t_p gb2, out = q + LN(zb2)
+        // wave 0: out = q + LN(zb2 + b2 - t_p gb2)
         if (w == 0) {
-            const float eg2 = e * g2;
-            gb2 += eg2;
-            const float sx = (red[0] + red[1]) + (red[2] + red[3]);
-            float z = ((part[0][c] + part[1][c]) + (part[2][c] + part[3][c])) + fmaf(-tp, gb2, b2);
-            z = fmaf(-tp * sx, eg2, z);
+            gb2 = fmaf(e, g2c, gb2);
+            const float z = ((part[0][c] + part[1][c]) + (part[2][c] + part[3][c])) + fmaf(-tp, gb2, b2);
             float s1 = z, s2 = z * z;
             wave_sum2(s1, s2);
             const float mu = s1 * (1.f / kD);
@@ -231,63 +264,51 @@ __global__ __launch_bounds__(256, 1) void mlp_token_kernel(MlpArgs a) {
             op[(int64_t)tok * a.out.sL + c] = from_f32<Tout>(qv + gam * (z - mu) * rs + bet);
         }
 
-        // unit f: the G2 step of its row (and, at the end of the mini-batch,
-        // the commit of W2's row); the LDS reads of g2 here end before the
-        // next token's barriers let wave 0 overwrite it
-        const bool commit = p == K - 1;
-        {
-            f32x4 *g2r = (f32x4 *)(G2c + (int64_t)f * kD);
-            f32x4 *w2r = (f32x4 *)(W2c + (int64_t)f * kD);
-            const float ex = e * x2;
-#pragma unroll 4
-            for (int m = 0; m < kD / 4; ++m) {
-                const f32x4 gv = *(const f32x4 *)&g2s[4 * m];
-                f32x4 gr = g2_zero ? f32x4{0.f, 0.f, 0.f, 0.f} : g2r[m];
+        if (p == K - 1) {
+            // commit the mini-batch's step (scaled by the last position's token_eta)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) gr[j] = fmaf(ex, gv[j], gr[j]);
-                if (commit) {
-                    f32x4 wr = w2r[m];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) wr[j] = fmaf(-tp, gr[j], wr[j]);
-                    w2r[m] = wr;
-                    gr = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
-                g2r[m] = gr;
-            }
-        }
-        if (commit) {
-#pragma unroll
-            for (int i = 0; i < kD; ++i) {
-                W1r[i] = fmaf(-tp, G1r[i], W1r[i]);
-                G1r[i] = 0.f;
+            for (int j = 0; j < kD; ++j) {
+                S[j] = fmaf(-tp, T[j], S[j]);
+                T[j] = 0.f;
             }
             b1 = fmaf(-tp, gb1, b1);
             gb1 = 0.f;
-            if (w == 0) {
-                b2 = fmaf(-tp, gb2, b2);
-                gb2 = 0.f;
-            }
+            b2 = fmaf(-tp, gb2, b2);
+            gb2 = 0.f;
             committed = true;
         }
-        __syncthreads();  // G2 and W2 rows stored before the next token reads them
     }
 
-    // write back W1 (after a commit), G1, and the biases
+    // write back what changed: W, b after a commit; the gradients unless they
+    // were clear in memory and are clear again
+    const bool g_clear_out = (a.pos0 + a.ntok) % K == 0;
     if (committed) {
+        if (unit_wave) {
 #pragma unroll
-        for (int i = 0; i < kD; ++i) W1c[i * kF + f] = W1r[i];
-        a.b1[(int64_t)ch * kF + f] = b1;
+            for (int j = 0; j < kD; ++j) W1c[j * kF + f] = S[j];
+            a.b1[(int64_t)ch * kF + f] = b1;
+        } else {
+#pragma unroll
+            for (int j = 0; j < kD; ++j) W2c[blk + j * kD] = S[j];
+        }
         if (w == 0) a.b2[cD + c] = b2;
     }
+    if (!(g_clear && g_clear_out)) {
+        if (unit_wave) {
 #pragma unroll
-    for (int i = 0; i < kD; ++i) G1c[i * kF + f] = G1r[i];
-    a.b1g[(int64_t)ch * kF + f] = gb1;
-    if (w == 0) a.b2g[cD + c] = gb2;
+            for (int j = 0; j < kD; ++j) G1c[j * kF + f] = T[j];
+            a.b1g[(int64_t)ch * kF + f] = gb1;
+        } else {
+#pragma unroll
+            for (int j = 0; j < kD; ++j) G2c[blk + j * kD] = T[j];
+        }
+        if (w == 0) a.b2g[cD + c] = gb2;
+    }
 }
 
 template <typename Tin, typename Tout>
 hipError_t launch_typed(const MlpArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL((mlp_token_kernel<Tin, Tout>), dim3(a.B * a.H), dim3(kF), 0, s, a);
+    hipLaunchKernelGGL((mlp_token_kernel<Tin, Tout>), dim3(a.B * a.H), dim3(512), 0, s, a);
     return hipGetLastError();
 }
 

@@ -59,6 +59,12 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
+// Orders a wave's LDS writes before its later LDS reads of values other lanes
+// wrote.  The hardware executes one wave's LDS accesses in program order, but
+// the compiler reasons per lane and may move a read above a write whose
+// address it proves different for that lane; this memory clobber stops it.
+__device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
+
 __device__ __forceinline__ float lane_value(float x, int lane) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }

@@ -108,6 +108,7 @@ __global__ __launch_bounds__(64, 2) void linear_token_kernel(LinearArgs a) {
             kr[j][c] = j < p0 ? kk[j] : 0.f;
             er[j][c] = j < p0 ? ee[j] : 0.f;
         }
+        wave_lds_order();
     } else if (g_clear) {
 #pragma unroll
         for (int i = 0; i < kD; ++i) Gs[i] = 0.f;
@@ -153,6 +154,7 @@ __global__ __launch_bounds__(64, 2) void linear_token_kernel(LinearArgs a) {
         // these writes (and the next token's writes follow these reads)
         sq[c] = qv;
         sk[c] = kv;
+        wave_lds_order();
 
         // z = k W + b at the mini-batch-start state (four interleaved chains)
         float z4[4] = {0.f, 0.f, 0.f, 0.f};
@@ -186,6 +188,7 @@ __global__ __launch_bounds__(64, 2) void linear_token_kernel(LinearArgs a) {
         if constexpr (ROWS) {
             kr[p][c] = kv;
             er[p][c] = eg;
+            wave_lds_order();
             // lane j <= p: q . k_j over the open rows, this token's included
             float sj = 0.f;
             if (c <= p) {

@@ -191,23 +191,20 @@ __global__ __launch_bounds__(512, 1) void mlp_token_kernel(MlpArgs a) {
         const float g2c = g2s[c];
         if (!unit_wave) {
             // g2 W2^T for unit 64v + c: row c of this wave's product tile, in
-            // two halves of 32 units.  The reads take values other lanes wrote:
-            // they rely on the wave's LDS accesses executing in program order,
-            // so the compiler must not move them across the writes (for one
-            // lane it can prove the addresses distinct): a memory clobber
-            // between the two.
+            // two halves of 32 units.  The reads take values other lanes wrote
+            // (wave_lds_order keeps them after the writes).
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
 #pragma unroll
                 for (int j = 0; j < kD / 2; ++j) tr[v][j][c] = S[32 * h + j] * g2c;
-                asm volatile("" ::: "memory");
+                wave_lds_order();
                 if ((c >> 5) == h) {
                     float d4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int k = 0; k < kD; ++k) d4[k & 3] += tr[v][c & 31][k];
                     dws[64 * v + c] = (d4[0] + d4[1]) + (d4[2] + d4[3]);
                 }
-                asm volatile("" ::: "memory");
+                wave_lds_order();
             }
             // the G2 step of the block: G2[u][c] += eta x2[u] g2[c]
             const float eg2c = e * g2c;

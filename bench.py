@@ -65,16 +65,24 @@ def decode_state_bytes(layout, positions):
     return total / len(positions)
 
 
-def mlp_decode_state_bytes(positions):
-    """Mean state bytes one TTT-MLP chain reads and writes per decode call
-    (dense gradients): W1, b1, W2, b2 read; W1_grad .. b2_grad read unless the
-    mini-batch is empty, and written; W1 .. b2 written by a call that closes
-    the mini-batch."""
+def mlp_decode_state_bytes(layout, positions):
+    """Mean state bytes one TTT-MLP chain reads and writes per decode call:
+    W1, b1, W2, b2 read, and written by a call that closes the mini-batch.
+    Dense layout: W1_grad .. b2_grad read unless the mini-batch is empty, and
+    written.  Rows layout: the p open rows [k | eta g1], [x2 | eta g2] and
+    b1_grad, b2_grad read, the row added (none when the call closes the
+    mini-batch) and b1_grad, b2_grad written."""
     par = (2 * D * F + F + D) * 4
+    row = 2 * (D + F) * 4
+    bias = (F + D) * 4
     total = 0
     for pos in positions:
         p = pos % K
-        n = par + (par if p else 0) + par
+        n = par
+        if layout == "dense":
+            n += (par if p else 0) + par
+        else:
+            n += p * row + (bias if p else 0) + (row if p != K - 1 else 0) + bias
         if p == K - 1:
             n += par
         total += n
@@ -106,8 +114,8 @@ def parse():
     ap.add_argument("--decode-eager", action="store_true",
                     help="decode workload: launch the decode calls one by one instead of replaying a HIP graph")
     ap.add_argument("--grad-layout", default="rows", choices=["rows", "dense"],
-                    help="decode workload: how the state holds the open mini-batch's gradient (the rows "
-                         "[k_j | eta_j g_j], or their dense sum W_grad)")
+                    help="decode workloads: how the state holds the open mini-batch's gradients (the rows "
+                         "[k_j | eta_j g_j], or their dense sums)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB twice (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -542,7 +550,7 @@ def bench_mlp_decode(args, w):
     dev = "cuda"
     B, H, P, T = w.B, w.H, w.prefill, w.decode
     inp = workload_inputs(w)
-    cfg = libttt.mlp_cfg(B, H, in_dtype=w.dtype, out_dtype=args.out_dtype)
+    cfg = libttt.mlp_cfg(B, H, in_dtype=w.dtype, out_dtype=args.out_dtype, grad_layout=args.grad_layout)
     odt = torch.float32 if args.out_dtype == "f32" else torch.bfloat16
     x = {n: inp[n].to(dev).contiguous() for n in ("XQ", "XK", "XV")}
     eta = inp["eta"].to(dev).contiguous()
@@ -585,18 +593,18 @@ def bench_mlp_decode(args, w):
     elapsed = run_steps(args, step)
     dec = stats(tm.ms("decode"))
     per_tok = linear_token_bytes(w.dtype, args.out_dtype)
-    state_rw = mlp_decode_state_bytes(range(P, P + T))
+    state_rw = mlp_decode_state_bytes(args.grad_layout, range(P, P + T))
     amount = (per_tok + state_rw) * B * H
     kms = {k: (v / T if k != "n" else v * T) for k, v in dec.items()}
     res = common(args, w, B * T / (dec["mean"] * 1e-3), elapsed, w.dtype,
-                 {"prefill": P, "decode_steps": T, "mlp_hidden": F,
+                 {"prefill": P, "decode_steps": T, "mlp_hidden": F, "grad_layout": args.grad_layout,
                   "decode_launch": f"HIP graph of the {T} decode calls, replayed; per-call time = replay time / {T}",
                   "decode_phase_ms": dec,
                   "value_is": f"decode tokens/s over the {T} decode calls (GPU time of the decode phase)"})
     res["metric"] = f"TTT-MLP decode tokens/sec ({w.name})"
     res["roofline"] = roofline("mlp_token_kernel", w.name, bound="hbm", amount=amount, kernel_ms=kms,
                                per_unit=f"{per_tok} B token in/out + {state_rw:g} B state read/write per chain "
-                                        "(dense gradients, mean over the decode positions)",
+                                        f"({args.grad_layout} gradients, mean over the decode positions)",
                                units=f"{B * H} chains, one token each")
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_mlp_decode(inp, w, args.cpu_seconds)

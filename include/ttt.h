@@ -193,12 +193,22 @@ typedef struct ttt_mlp_cfg {
     int32_t rope;
     float rope_base;
     float ln_eps;
+    int32_t grad_layout; /* ttt_grad_layout of the *_grad state (0: dense) */
 } ttt_mlp_cfg;
 
 /* Carried state of TTT-MLP (fp32, device, contiguous):
  *   W1 [B, H, D, F], b1 [B, H, F], W2 [B, H, F, D], b2 [B, H, D],
  *   W1_grad, b1_grad, W2_grad, b2_grad of the same shapes (open mini-batch),
- *   offset (host). */
+ *   offset (host).
+ * The open mini-batch's gradient sums are G1 = sum_j k_j^T (eta_j g1_j) and
+ * G2 = sum_j x2_j^T (eta_j g2_j) (x2_j = GELU(k_j W1 + b1) at the mini-batch
+ * start).  In TTT_GRAD_DENSE, W1_grad and W2_grad hold G1 and G2.  In
+ * TTT_GRAD_ROWS they hold the rows that make them up: per chain W1_grad is
+ * read as [D*F / (D+F), D+F] with row j = [k_j (D) | eta_j g1_j (F)], and
+ * W2_grad as rows [x2_j (F) | eta_j g2_j (D)], for j < offset % K (rows past
+ * that are undefined).  b1_grad, b2_grad are dense in both layouts.  The
+ * rows layout keeps a decode call's state traffic at W1, W2 plus ~2.5 KB per
+ * open token instead of W1, W2 and both dense gradients read and written. */
 typedef struct ttt_mlp_state {
     float *W1, *b1, *W2, *b2;
     float *W1_grad, *b1_grad, *W2_grad, *b2_grad;

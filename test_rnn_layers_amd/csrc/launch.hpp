@@ -27,6 +27,7 @@ struct MlpArgs {
     const float *te;  // token_eta [K] or nullptr (all ones)
     int32_t K;        // mini-batch size (token kernel; the dual kernel takes 16)
     int32_t ntok;     // tokens (token kernel)
+    int32_t grad_rows;  // W1_grad / W2_grad hold the open rows [k | eta g1], [x2 | eta g2]
 };
 
 hipError_t launch_linear_token(const LinearArgs &a, int in_bf16, int out_bf16, hipStream_t s);

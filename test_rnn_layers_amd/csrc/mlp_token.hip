@@ -29,6 +29,10 @@
 // The two roles keep their state in the same two register arrays.  A call
 // reads and writes the state once; per token it reads q, k, v, eta and
 // writes one output row.
+// ROWS: the gradient state holds the open mini-batch's rows [k_j | eta_j g1_j]
+// and [x2_j | eta_j g2_j] instead of G1 and G2.  The call rebuilds its dense
+// G1 columns and G2 blocks in registers from the rows (while W1, W2 are still
+// arriving), runs as above, and stores only the rows its tokens add.
 #include "device_common.hpp"
 #include "gelu.hpp"
 #include "launch.hpp"
@@ -37,8 +41,9 @@ namespace ttt {
 namespace {
 
 constexpr int kF = 256;
+constexpr int kRow = kD + kF;  // floats per gradient row, both layers
 
-template <typename Tin, typename Tout>
+template <typename Tin, typename Tout, bool ROWS>
 __global__ __launch_bounds__(512, 1) void mlp_token_kernel(MlpArgs a) {
     const int ch = blockIdx.x;
     const int bi = ch / a.H, hi = ch % a.H;
@@ -52,7 +57,11 @@ __global__ __launch_bounds__(512, 1) void mlp_token_kernel(MlpArgs a) {
     __shared__ float dws[kF];          // (g2 W2^T)[u]
     __shared__ float g2s[kD];
     __shared__ float part[4][kD];
-    __shared__ float tr[4][kD / 2][kD + 1];  // per block wave: products W2[64v + j][c] g2[c] at [j mod 32][c]
+    // per block wave: products W2[64v + j][c] g2[c] at [j mod 32][c]; in the
+    // rows layout first the open rows' x2 (before the token loop)
+    __shared__ __align__(16) float trbuf[4 * (kD / 2) * (kD + 1)];
+    float (*tr)[kD / 2][kD + 1] = reinterpret_cast<float (*)[kD / 2][kD + 1]>(trbuf);
+    __shared__ __align__(16) float kr[ROWS ? 16 : 1][kD];  // ROWS: the open rows' k
     __shared__ float rcs[16][kD], rsn[16][kD];
 
     const int64_t cD = (int64_t)ch * kD;
@@ -80,7 +89,7 @@ __global__ __launch_bounds__(512, 1) void mlp_token_kernel(MlpArgs a) {
 #pragma unroll
         for (int j = 0; j < kD; ++j) S[j] = W2c[blk + j * kD];
     }
-    if (g_clear) {
+    if (g_clear || ROWS) {
 #pragma unroll
         for (int j = 0; j < kD; ++j) T[j] = 0.f;
     } else if (unit_wave) {
@@ -106,6 +115,37 @@ __global__ __launch_bounds__(512, 1) void mlp_token_kernel(MlpArgs a) {
     // token_eta of position c of the mini-batch (lanes c < K of every wave), 1 without it
     const float te_c = (a.te != nullptr && c < K) ? a.te[c] : 1.f;
     bool committed = false;  // W, b change only at a commit
+
+    if constexpr (ROWS) {
+        if (!g_clear) {
+            // the open rows j < p0: unit thread f needs eta_j g1_j[f], block
+            // thread (v, c) needs eta_j g2_j[c] (registers); k_j and x2_j are
+            // read by many threads (LDS)
+            float e[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (j < p0) e[j] = unit_wave ? G1c[j * kRow + kD + f] : G2c[j * kRow + kF + c];
+            float *x2r = trbuf;  // [16][kF]
+            for (int i = threadIdx.x; i < p0 * kF; i += 512) x2r[i] = G2c[(i / kF) * kRow + (i % kF)];
+            if (w == 0)
+                for (int j = 0; j < p0; ++j) kr[j][c] = G1c[j * kRow + c];
+            __syncthreads();
+            // G1[:, f] = sum_j k_j eta_j g1_j[f];  G2[64v + u][c] = sum_j x2_j[64v + u] eta_j g2_j[c]
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                if (j < p0) {
+                    const float *src = unit_wave ? &kr[j][0] : &x2r[j * kF + 64 * v];
+#pragma unroll
+                    for (int i = 0; i < kD; i += 4) {
+                        const f32x4 r4 = *(const f32x4 *)&src[i];
+#pragma unroll
+                        for (int l = 0; l < 4; ++l) T[i + l] = fmaf(r4[l], e[j], T[i + l]);
+                    }
+                }
+            }
+            __syncthreads();  // the x2 rows are read before the buffer becomes the product tile
+        }
+    }
 
     if (a.rope && w == 0) {
         // angle p * base^(-2i/D) for the pair (i, i + 32) holding column c, at
@@ -138,6 +178,8 @@ __global__ __launch_bounds__(512, 1) void mlp_token_kernel(MlpArgs a) {
             }
             sq[c] = qv;
             sk[c] = kv;
+            // ROWS: this token's row of k, unless it closes the mini-batch
+            if (ROWS && p != K - 1) G1c[p * kRow + c] = kv;
         }
         __syncthreads();
 
@@ -154,6 +196,7 @@ __global__ __launch_bounds__(512, 1) void mlp_token_kernel(MlpArgs a) {
             const Gelu gz = gelu_both((z4[0] + z4[1]) + (z4[2] + z4[3]));
             x2s[f] = gz.g;
             dg = gz.dg;
+            if (ROWS && p != K - 1) G2c[p * kRow + f] = gz.g;
         }
         __syncthreads();
 
@@ -222,6 +265,7 @@ __global__ __launch_bounds__(512, 1) void mlp_token_kernel(MlpArgs a) {
         if (unit_wave) {
             const float eg1 = e * (dws[f] * dg);
             gb1 += eg1;
+            if (ROWS && p != K - 1) G1c[p * kRow + kD + f] = eg1;
             float zb4[4] = {fmaf(-tp, gb1, b1), 0.f, 0.f, 0.f};
 #pragma unroll
             for (int i = 0; i < kD; i += 4) {
@@ -253,6 +297,7 @@ __global__ __launch_bounds__(512, 1) void mlp_token_kernel(MlpArgs a) {
         // wave 0: out = q + LN(zb2 + b2 - t_p gb2)
         if (w == 0) {
             gb2 = fmaf(e, g2c, gb2);
+            if (ROWS && p != K - 1) G2c[p * kRow + kF + c] = e * g2c;
             const float z = ((part[0][c] + part[1][c]) + (part[2][c] + part[3][c])) + fmaf(-tp, gb2, b2);
             float s1 = z, s2 = z * z;
             wave_sum2(s1, s2);
@@ -292,10 +337,12 @@ __global__ __launch_bounds__(512, 1) void mlp_token_kernel(MlpArgs a) {
     }
     if (!(g_clear && g_clear_out)) {
         if (unit_wave) {
+            if (!ROWS) {
 #pragma unroll
-            for (int j = 0; j < kD; ++j) G1c[j * kF + f] = T[j];
+                for (int j = 0; j < kD; ++j) G1c[j * kF + f] = T[j];
+            }
             a.b1g[(int64_t)ch * kF + f] = gb1;
-        } else {
+        } else if (!ROWS) {
 #pragma unroll
             for (int j = 0; j < kD; ++j) G2c[blk + j * kD] = T[j];
         }
@@ -305,7 +352,10 @@ __global__ __launch_bounds__(512, 1) void mlp_token_kernel(MlpArgs a) {
 
 template <typename Tin, typename Tout>
 hipError_t launch_typed(const MlpArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL((mlp_token_kernel<Tin, Tout>), dim3(a.B * a.H), dim3(512), 0, s, a);
+    if (a.grad_rows)
+        hipLaunchKernelGGL((mlp_token_kernel<Tin, Tout, true>), dim3(a.B * a.H), dim3(512), 0, s, a);
+    else
+        hipLaunchKernelGGL((mlp_token_kernel<Tin, Tout, false>), dim3(a.B * a.H), dim3(512), 0, s, a);
     return hipGetLastError();
 }
 

@@ -160,6 +160,8 @@ ttt_status check_mlp_cfg(const ttt_mlp_cfg *cfg) {
                           cfg->rope_base, cfg->rope)))
         return s;
     if (cfg->F != 256) return fail(TTT_ERR_SHAPE, "MLP hidden width F=%d unsupported (must be 256)", cfg->F);
+    if (cfg->grad_layout != TTT_GRAD_DENSE && cfg->grad_layout != TTT_GRAD_ROWS)
+        return fail(TTT_ERR_UNSUPPORTED, "unknown grad_layout %d", (int)cfg->grad_layout);
     return TTT_OK;
 }
 
@@ -311,11 +313,19 @@ ttt_status mlp_call(Mode mode, const ttt_mlp_cfg *cfg, int32_t L, const Act &x, 
     a.eps = cfg->ln_eps;
     const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     const int in_bf16 = cfg->in_dtype == TTT_BF16, out_bf16 = cfg->out_dtype == TTT_BF16;
+    a.grad_rows = cfg->grad_layout == TTT_GRAD_ROWS;
     const int K = cfg->K;
-    int head = L, rest = 0;  // token kernel for `head` tokens, then the dual kernel for `rest`
+    // token kernel for `head` tokens, the dual kernel for `body` tokens, the
+    // token kernel again for `tail` (the dual kernel leaves a trailing open
+    // mini-batch in the dense layout only)
+    int head = L, body = 0, tail = 0;
     if (mode == Mode::Prefill && K == 16 && in_bf16) {
         head = (int)std::min<int64_t>(L, (K - st->offset % K) % K);
-        rest = L - head;
+        body = L - head;
+        if (a.grad_rows) {
+            tail = body % K;
+            body -= tail;
+        }
     }
     hipError_t e;
     if (head > 0) {
@@ -324,12 +334,18 @@ ttt_status mlp_call(Mode mode, const ttt_mlp_cfg *cfg, int32_t L, const Act &x, 
         a.pos0 = st->offset;
         if ((e = launch_mlp_token(a, in_bf16, out_bf16, hs)) != hipSuccess) return hip_fail(e, "mlp token kernel");
     }
-    if (rest > 0) {
-        a.nblk = (rest + K - 1) / K;
-        a.tail = rest % K;
+    if (body > 0) {
+        a.nblk = (body + K - 1) / K;
+        a.tail = body % K;
         a.t0 = head;
         a.pos0 = st->offset + head;
         if ((e = launch_mlp_dual(a, in_bf16, out_bf16, hs)) != hipSuccess) return hip_fail(e, "mlp kernel");
+    }
+    if (tail > 0) {
+        a.ntok = tail;
+        a.t0 = L - tail;
+        a.pos0 = st->offset + (L - tail);
+        if ((e = launch_mlp_token(a, in_bf16, out_bf16, hs)) != hipSuccess) return hip_fail(e, "mlp token kernel");
     }
     st->offset += L;
     return ok();

@@ -44,7 +44,7 @@ class ttt_linear_state(ctypes.Structure):
 class ttt_mlp_cfg(ctypes.Structure):
     _fields_ = [("B", c_int32), ("H", c_int32), ("D", c_int32), ("F", c_int32), ("K", c_int32),
                 ("in_dtype", c_int32), ("out_dtype", c_int32), ("rope", c_int32), ("rope_base", c_float),
-                ("ln_eps", c_float)]
+                ("ln_eps", c_float), ("grad_layout", c_int32)]
 
 
 class ttt_mlp_state(ctypes.Structure):
@@ -211,8 +211,10 @@ def linear_cfg(B, H, *, K=16, in_dtype="bf16", out_dtype="f32", rope=False, rope
 
 
 def mlp_cfg(B, H, *, F=256, K=16, in_dtype="bf16", out_dtype="f32", rope=False, rope_base=10000.0, ln_eps=1e-6,
-            D=64):
-    return ttt_mlp_cfg(B, H, D, F, K, dtype_code(in_dtype), dtype_code(out_dtype), int(rope), rope_base, ln_eps)
+            D=64, grad_layout="dense"):
+    layout = {"dense": TTT_GRAD_DENSE, "rows": TTT_GRAD_ROWS}.get(grad_layout, grad_layout)
+    return ttt_mlp_cfg(B, H, D, F, K, dtype_code(in_dtype), dtype_code(out_dtype), int(rope), rope_base, ln_eps,
+                       int(layout))
 
 
 # ---------------------------------------------------------------------------

@@ -98,11 +98,13 @@ class MlpGPU:
     """One TTT-MLP problem on the GPU: device inputs, state, out."""
 
     def __init__(self, inp: dict, *, K=16, rope=False, out_dtype="f32", device="cuda", token_eta=None,
-                 in_dtype="bf16"):
+                 in_dtype="bf16", grad_layout="dense"):
         B, H, L, D = inp["XQ"].shape
         F = inp["W1"].shape[-1]
         self.B, self.H, self.L, self.D, self.F = B, H, L, D, F
-        self.cfg = libttt.mlp_cfg(B, H, F=F, K=K, in_dtype=in_dtype, out_dtype=out_dtype, rope=rope)
+        self.grad_layout = grad_layout
+        self.cfg = libttt.mlp_cfg(B, H, F=F, K=K, in_dtype=in_dtype, out_dtype=out_dtype, rope=rope,
+                                  grad_layout=grad_layout)
         self.te = None if token_eta is None else torch.tensor(np.asarray(token_eta), dtype=torch.float32,
                                                               device=device)
         self.x = {n: inp[n].to(device).contiguous() for n in ("XQ", "XK", "XV")}
@@ -122,8 +124,18 @@ class MlpGPU:
                                self.out[:, :, sl], token_eta=self.te)
 
     def result(self):
+        """out and the 8 state arrays; in the rows layout the dense W1_grad,
+        W2_grad are rebuilt from the open rows (sum of outer products)."""
         torch.cuda.synchronize()
-        return (to_f64(self.out),) + tuple(to_f64(t) for t in self.state.tensors)
+        st = [to_f64(t) for t in self.state.tensors]
+        if self.grad_layout == "rows":
+            B, H, D, F = self.B, self.H, self.D, self.F
+            n = self.state.offset % self.cfg.K
+            r1 = st[4].reshape(B, H, -1)[:, :, : 16 * (D + F)].reshape(B, H, 16, D + F)[:, :, :n]
+            r2 = st[6].reshape(B, H, -1)[:, :, : 16 * (F + D)].reshape(B, H, 16, F + D)[:, :, :n]
+            st[4] = np.einsum("bhji,bhjf->bhif", r1[..., :D], r1[..., D:])
+            st[6] = np.einsum("bhjf,bhjc->bhfc", r2[..., :F], r2[..., F:])
+        return (to_f64(self.out),) + tuple(st)
 
 
 def oracle_mlp(inp: dict, *, K=16, rope=False, chains=None, L=None, token_eta=None):

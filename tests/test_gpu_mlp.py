@@ -38,9 +38,10 @@ def _compare(name, got, ref, chains, *, out_dtype="f32", tol=TOL_BF16):
 
 
 def _run(name, inp, *, rope=False, pieces=(), out_dtype="f32", chains=None, token_eta=None, K=16, in_dtype="bf16",
-         decode=(), tol=TOL_BF16):
+         decode=(), tol=TOL_BF16, grad_layout="dense"):
     B, H, L, D = inp["XQ"].shape
-    g = MlpGPU(inp, rope=rope, out_dtype=out_dtype, token_eta=token_eta, K=K, in_dtype=in_dtype)
+    g = MlpGPU(inp, rope=rope, out_dtype=out_dtype, token_eta=token_eta, K=K, in_dtype=in_dtype,
+               grad_layout=grad_layout)
     cuts = [0] + list(pieces) + [L]
     for i in range(len(cuts) - 1):
         g.run(cuts[i], cuts[i + 1], decode=cuts[i] in decode)
@@ -189,4 +190,57 @@ def test_decode_workload_sampled():
     B, H, L = w.B, w.H, w.L
     cuts = [w.prefill] + list(range(w.prefill + 1, L))
     _run(w.name, inp, pieces=cuts, decode=set(cuts), chains=[(0, 0), (7, 5), (B - 1, H - 1)])
+
+
+# --- the rows layout of the gradients (open rows [k | eta g1], [x2 | eta g2])
+def test_rows_decode_steps():
+    inp = make_inputs(2, 2, 52, dtype="bf16", seed=191, rich=True, mlp_hidden=256)
+    cuts = [20] + list(range(21, 52))
+    _run("mlp_rows_decode", inp, rope=True, pieces=cuts, decode=set(cuts), grad_layout="rows")
+
+
+def test_rows_prefill_pieces():
+    """Open heads and tails around dual-kernel bodies, in the rows layout."""
+    inp = make_inputs(2, 3, 90, dtype="bf16", seed=192, rich=True, mlp_hidden=256)
+    _run("mlp_rows_pieces", inp, pieces=(5, 21, 40, 41, 75), grad_layout="rows")
+
+
+@pytest.mark.parametrize("K", [1, 8])
+def test_rows_other_minibatch_sizes(K):
+    inp = make_inputs(1, 2, 30, dtype="f32", seed=193 + K, rich=True, mlp_hidden=256)
+    _run(f"mlp_rows_K{K}", inp, in_dtype="f32", K=K, pieces=(7, 13), tol=1e-4, grad_layout="rows")
+
+
+def test_rows_decode_token_eta():
+    r = np.random.default_rng(15)
+    te = (1.0 / np.arange(1, 17) + 0.05 * r.uniform(size=16)).astype(np.float32).astype(np.float64)
+    inp = make_inputs(1, 3, 40, dtype="bf16", seed=195, rich=True, mlp_hidden=256)
+    cuts = [9] + list(range(10, 40))
+    _run("mlp_rows_decode_token_eta", inp, pieces=cuts, decode=set(cuts), token_eta=te, grad_layout="rows")
+
+
+def test_rows_matches_dense():
+    """The same calls in both layouts agree to the bf16 bar.  (Not to fp32
+    rounding: in the rows layout the prefill's trailing partial mini-batch runs
+    in the fp32 token kernel, in the dense layout in the fp16-operand dual
+    kernel.)"""
+    inp = make_inputs(2, 2, 45, dtype="bf16", seed=196, rich=True, mlp_hidden=256)
+    res = []
+    for layout in ("dense", "rows"):
+        g = MlpGPU(inp, grad_layout=layout)
+        g.run(0, 23)
+        for t in range(23, 45):
+            g.run(t, t + 1, decode=True)
+        res.append(g.result())
+    for x, y in zip(res[0], res[1]):
+        assert max_abs(x, y) <= TOL_BF16, max_abs(x, y)
+
+
+def test_rows_decode_workload_sampled():
+    w = next(x for x in WORKLOADS if x.kind == "mlp_decode")
+    inp = workload_inputs(w)
+    B, H, L = w.B, w.H, w.L
+    cuts = [w.prefill] + list(range(w.prefill + 1, L))
+    _run(w.name + "_rows", inp, pieces=cuts, decode=set(cuts), chains=[(0, 0), (7, 5), (B - 1, H - 1)],
+         grad_layout="rows")
 

@@ -3,9 +3,27 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <cstdint>
+
 #include "device_common.hpp"
 
 namespace ttt {
+
+// Raises a kernel's dynamic LDS limit to `bytes` once per device (the limit
+// is per device), safe under concurrent callers: `done` holds one bit per
+// device ordinal < 64 (a concurrent first call may set it twice, which is
+// harmless); devices past 63 set it on every launch.
+inline hipError_t ensure_lds_limit(const void *fn, size_t bytes, std::atomic<uint64_t> &done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
 
 // Everything a TTT-MLP launch needs (state [B*H, ...] fp32, F = 256).
 struct MlpArgs {

@@ -676,12 +676,8 @@ template <typename Tin, typename Tout, typename T, bool ROPE, bool TE>
 hipError_t launch_typed(const LinearArgs &a, hipStream_t s) {
     const void *fn = (const void *)&linear_dual_kernel<Tin, Tout, T, ROPE, TE>;
     const size_t lds = sizeof(Smem<T>);
-    static bool configured = false;  // per instantiation
-    if (!configured) {
-        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        configured = true;
-    }
+    static std::atomic<uint64_t> configured{0};  // per instantiation: devices whose LDS limit is raised
+    if (hipError_t e = ensure_lds_limit(fn, lds, configured); e != hipSuccess) return e;
     hipLaunchKernelGGL((linear_dual_kernel<Tin, Tout, T, ROPE, TE>), dim3(a.B * a.H), dim3(512), lds, s, a);
     return hipGetLastError();
 }

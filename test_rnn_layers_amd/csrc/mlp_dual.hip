@@ -503,12 +503,8 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
 template <typename Tin, typename Tout, bool ROPE>
 hipError_t launch_typed(const MlpArgs &a, hipStream_t s) {
     const void *fn = (const void *)&mlp_dual_kernel<Tin, Tout, ROPE>;
-    static bool configured = false;
-    if (!configured) {
-        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Smem));
-        if (e != hipSuccess) return e;
-        configured = true;
-    }
+    static std::atomic<uint64_t> configured{0};  // per instantiation: devices whose LDS limit is raised
+    if (hipError_t e = ensure_lds_limit(fn, sizeof(Smem), configured); e != hipSuccess) return e;
     hipLaunchKernelGGL((mlp_dual_kernel<Tin, Tout, ROPE>), dim3(a.B * a.H), dim3(512), sizeof(Smem), s, a);
     return hipGetLastError();
 }

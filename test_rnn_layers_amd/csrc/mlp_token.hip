@@ -455,12 +455,8 @@ template <typename Tin, typename Tout, bool ROWS>
 hipError_t launch_layout(const MlpArgs &a, hipStream_t s) {
     const void *fn = (const void *)&mlp_token_kernel<Tin, Tout, ROWS>;
     const size_t lds = sizeof(TokSmem<ROWS>);
-    static bool configured = false;  // per instantiation
-    if (!configured) {
-        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        configured = true;
-    }
+    static std::atomic<uint64_t> configured{0};  // per instantiation: devices whose LDS limit is raised
+    if (hipError_t e = ensure_lds_limit(fn, lds, configured); e != hipSuccess) return e;
     hipLaunchKernelGGL((mlp_token_kernel<Tin, Tout, ROWS>), dim3(a.B * a.H), dim3(512), lds, s, a);
     return hipGetLastError();
 }

@@ -150,6 +150,15 @@ def test_token_eta_other_minibatch_size():
     _check_full("token_eta_K13", inp, dtype="f32", K=13, pieces=[7, 20], token_eta=_token_eta(13, 5))
 
 
+def test_rows_layout_token_eta_K13_rope():
+    """Rows layout, a mini-batch size the dual kernel does not take, rotary and
+    token_eta together, with open pieces and decode calls."""
+    inp = make_inputs(2, 2, 45, dtype="bf16", seed=79, rich=True)
+    cuts = [6, 20] + list(range(21, 45))
+    _check_full("rows_K13_rope_token_eta", inp, dtype="bf16", K=13, rope=True, pieces=cuts, decode=set(cuts[2:]),
+                grad_layout="rows", token_eta=_token_eta(13, 6))
+
+
 def test_constant_token_eta_equals_scaled_eta():
     """On the GPU: token_eta = c everywhere gives the outputs of token_eta
     absent with every learning rate times c.  c = 0.5 scales exactly, so on

@@ -219,6 +219,16 @@ def test_rows_decode_token_eta():
     _run("mlp_rows_decode_token_eta", inp, pieces=cuts, decode=set(cuts), token_eta=te, grad_layout="rows")
 
 
+def test_rows_K8_fp32_token_eta_rope():
+    """Rows layout with fp32 inputs, K = 8, rotary and token_eta together."""
+    r = np.random.default_rng(8)
+    te = 1.0 / np.arange(1, 9) + 0.05 * r.uniform(size=8)
+    inp = make_inputs(1, 2, 30, dtype="f32", seed=197, rich=True, mlp_hidden=256)
+    cuts = [5, 11] + list(range(12, 30))
+    _run("mlp_rows_K8_f32_te_rope", inp, in_dtype="f32", K=8, rope=True, pieces=cuts, decode=set(cuts[2:]),
+         token_eta=te, tol=1e-4, grad_layout="rows")
+
+
 def test_rows_matches_dense():
     """The same calls in both layouts agree to the bf16 bar.  (Not to fp32
     rounding: in the rows layout the prefill's trailing partial mini-batch runs
@@ -243,4 +253,46 @@ def test_rows_decode_workload_sampled():
     cuts = [w.prefill] + list(range(w.prefill + 1, L))
     _run(w.name + "_rows", inp, pieces=cuts, decode=set(cuts), chains=[(0, 0), (7, 5), (B - 1, H - 1)],
          grad_layout="rows")
+
+
+@pytest.mark.parametrize("grad_layout", ["dense", "rows"])
+def test_decode_graph_replays_match_eager(grad_layout):
+    """TTT-MLP decode calls captured in a HIP graph and replayed (as the
+    benchmark runs them): every replay, with eager work and synchronisation
+    in between, reproduces the eager outputs and final state bit for bit."""
+    inp = make_inputs(2, 2, 40, dtype="bf16", seed=161, rich=True, mlp_hidden=256)
+    P, T = 13, 20  # the prefill ends inside a mini-batch; decode crosses a boundary
+
+    def fresh():
+        g = MlpGPU(inp, grad_layout=grad_layout)
+        g.run(0, P)
+        return g
+
+    def decode_calls(g):
+        for t in range(P, P + T):
+            g.run(t, t + 1, decode=True)
+
+    ref = fresh()
+    decode_calls(ref)
+    want = ref.result()
+
+    g = fresh()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        decode_calls(g)
+    torch.cuda.synchronize()
+    saved = [t.clone() for t in g.state.tensors]  # post-prefill state
+    for rep in range(3):
+        # eager work between replays: restore the post-prefill state, clear the outputs
+        for dst, src in zip(g.state.tensors, saved):
+            dst.copy_(src)
+        g.out[:, :, P:].fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = g.result()
+        assert np.array_equal(got[0][:, :, P:P + T], want[0][:, :, P:P + T]), rep
+        for a, b in zip(got[1:], want[1:]):
+            assert np.array_equal(a, b), rep
 

@@ -52,6 +52,16 @@ hipError_t launch_linear_token(const LinearArgs &a, int in_bf16, int out_bf16, h
 hipError_t launch_linear_dual(const LinearArgs &a, int in_bf16, int out_bf16, hipStream_t s);
 hipError_t launch_mlp_dual(const MlpArgs &a, int in_bf16, int out_bf16, hipStream_t s);
 hipError_t launch_mlp_token(const MlpArgs &a, int in_bf16, int out_bf16, hipStream_t s);
-hipError_t launch_tile(float *dst, const float *src, int64_t per, int64_t total, hipStream_t s);
+// State initialisation: up to 8 segments filled by one launch.
+struct TileSeg {
+    float *dst;
+    const float *src;  // [per] tiled over dst[total]; nullptr: zeros
+    int64_t per, total;
+};
+struct TileList {
+    TileSeg seg[8];
+    int32_t n;
+};
+hipError_t launch_tiles(const TileList &t, hipStream_t s);
 
 }  // namespace ttt

@@ -21,6 +21,8 @@
 // Used for decoding, for the tokens that complete an open mini-batch before a
 // prefill, for a trailing partial mini-batch, and for mini-batch sizes the
 // dual-form MFMA kernel does not take.
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -287,11 +289,21 @@ __global__ __launch_bounds__(64, 2) void linear_token_kernel(LinearArgs a) {
     if (!(g_clear && g_clear_out)) a.bg[(int64_t)ch * kD + c] = gbs;
 }
 
-// dst[b, i] = src[i % per] for b < copies: tiles a per-head parameter over the
-// batch; with src == nullptr it writes zeros.
-__global__ void tile_kernel(float *dst, const float *src, int64_t per, int64_t total) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < total) dst[i] = src ? src[i % per] : 0.f;
+// Segment y of one launch: dst[i] = src[i % per] for i < total (a per-head
+// parameter tiled over the batch), or zeros with src == nullptr.  VEC: every
+// pointer 16-byte aligned and per, total multiples of 4 (float4 accesses).
+template <bool VEC>
+__global__ void tile_kernel(TileList t) {
+    const TileSeg sg = t.seg[blockIdx.y];
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    if constexpr (VEC) {
+        const int64_t n4 = sg.total / 4, p4 = sg.per >= 4 ? sg.per / 4 : 1;
+        for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+            ((float4 *)sg.dst)[i] = sg.src ? ((const float4 *)sg.src)[i % p4] : float4{0.f, 0.f, 0.f, 0.f};
+    } else {
+        for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < sg.total; i += stride)
+            sg.dst[i] = sg.src ? sg.src[i % sg.per] : 0.f;
+    }
 }
 
 template <bool ROWS>
@@ -315,10 +327,24 @@ hipError_t launch_linear_token(const LinearArgs &a, int in_bf16, int out_bf16, h
     return hipGetLastError();
 }
 
-hipError_t launch_tile(float *dst, const float *src, int64_t per, int64_t total, hipStream_t s) {
-    if (total <= 0) return hipSuccess;
-    const int64_t nb = (total + 255) / 256;
-    hipLaunchKernelGGL(tile_kernel, dim3((unsigned)nb), dim3(256), 0, s, dst, src, per, total);
+hipError_t launch_tiles(const TileList &t, hipStream_t s) {
+    if (t.n <= 0) return hipSuccess;
+    int64_t most = 0;
+    bool vec = true;
+    for (int i = 0; i < t.n; ++i) {
+        const TileSeg &g = t.seg[i];
+        most = g.total > most ? g.total : most;
+        vec = vec && (g.src == nullptr || g.per % 4 == 0) && g.total % 4 == 0 && ((uintptr_t)g.dst & 15) == 0 &&
+              ((uintptr_t)g.src & 15) == 0;
+    }
+    const int64_t items = vec ? most / 4 : most;
+    const int64_t nb = std::min<int64_t>((items + 255) / 256, 2048);
+    if (nb <= 0) return hipSuccess;
+    const dim3 grid((unsigned)nb, (unsigned)t.n);
+    if (vec)
+        hipLaunchKernelGGL(tile_kernel<true>, grid, dim3(256), 0, s, t);
+    else
+        hipLaunchKernelGGL(tile_kernel<false>, grid, dim3(256), 0, s, t);
     return hipGetLastError();
 }
 

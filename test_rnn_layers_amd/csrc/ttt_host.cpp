@@ -384,11 +384,13 @@ ttt_status ttt_linear_state_init(const ttt_linear_cfg *cfg, const float *W0, con
     if ((s = check_linear_state(cfg, state, sr, false))) return s;
     const int64_t H = cfg->H, D = cfg->D, n = (int64_t)cfg->B * H;
     const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e;
-    if ((e = launch_tile(state->W, W0, H * D * D, n * D * D, hs)) != hipSuccess) return hip_fail(e, "tile W");
-    if ((e = launch_tile(state->b, b0, H * D, n * D, hs)) != hipSuccess) return hip_fail(e, "tile b");
-    if ((e = launch_tile(state->W_grad, nullptr, 1, n * D * D, hs)) != hipSuccess) return hip_fail(e, "zero W_grad");
-    if ((e = launch_tile(state->b_grad, nullptr, 1, n * D, hs)) != hipSuccess) return hip_fail(e, "zero b_grad");
+    TileList t{};
+    t.seg[0] = TileSeg{state->W, W0, H * D * D, n * D * D};
+    t.seg[1] = TileSeg{state->b, b0, H * D, n * D};
+    t.seg[2] = TileSeg{state->W_grad, nullptr, 1, n * D * D};
+    t.seg[3] = TileSeg{state->b_grad, nullptr, 1, n * D};
+    t.n = 4;
+    if (hipError_t e = launch_tiles(t, hs); e != hipSuccess) return hip_fail(e, "state init");
     state->offset = 0;
     return ok();
 }
@@ -414,15 +416,17 @@ ttt_status ttt_mlp_state_init(const ttt_mlp_cfg *cfg, const float *W1, const flo
     if ((s = check_mlp_state(cfg, state, sr, false))) return s;
     const int64_t H = cfg->H, D = cfg->D, F = cfg->F, n = (int64_t)cfg->B * H;
     const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e;
-    if ((e = launch_tile(state->W1, W1, H * D * F, n * D * F, hs)) != hipSuccess) return hip_fail(e, "tile W1");
-    if ((e = launch_tile(state->b1, b1, H * F, n * F, hs)) != hipSuccess) return hip_fail(e, "tile b1");
-    if ((e = launch_tile(state->W2, W2, H * F * D, n * F * D, hs)) != hipSuccess) return hip_fail(e, "tile W2");
-    if ((e = launch_tile(state->b2, b2, H * D, n * D, hs)) != hipSuccess) return hip_fail(e, "tile b2");
-    if ((e = launch_tile(state->W1_grad, nullptr, 1, n * D * F, hs)) != hipSuccess) return hip_fail(e, "zero W1_grad");
-    if ((e = launch_tile(state->b1_grad, nullptr, 1, n * F, hs)) != hipSuccess) return hip_fail(e, "zero b1_grad");
-    if ((e = launch_tile(state->W2_grad, nullptr, 1, n * F * D, hs)) != hipSuccess) return hip_fail(e, "zero W2_grad");
-    if ((e = launch_tile(state->b2_grad, nullptr, 1, n * D, hs)) != hipSuccess) return hip_fail(e, "zero b2_grad");
+    TileList t{};
+    t.seg[0] = TileSeg{state->W1, W1, H * D * F, n * D * F};
+    t.seg[1] = TileSeg{state->b1, b1, H * F, n * F};
+    t.seg[2] = TileSeg{state->W2, W2, H * F * D, n * F * D};
+    t.seg[3] = TileSeg{state->b2, b2, H * D, n * D};
+    t.seg[4] = TileSeg{state->W1_grad, nullptr, 1, n * D * F};
+    t.seg[5] = TileSeg{state->b1_grad, nullptr, 1, n * F};
+    t.seg[6] = TileSeg{state->W2_grad, nullptr, 1, n * F * D};
+    t.seg[7] = TileSeg{state->b2_grad, nullptr, 1, n * D};
+    t.n = 8;
+    if (hipError_t e = launch_tiles(t, hs); e != hipSuccess) return hip_fail(e, "state init");
     state->offset = 0;
     return ok();
 }

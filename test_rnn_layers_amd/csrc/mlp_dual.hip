@@ -407,8 +407,9 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const f32x4 z = mfma16(M2, G2[r], mfma32(xb2p, pair_b(W2s[0][r], W2s[1][r]), zero));
+                const float b2v = w == 0 ? sm.b2[16 * r + n] : 0.f;  // b2 (current) rides in slice 0
 #pragma unroll
-                for (int j = 0; j < 4; ++j) sm.part[w][4 * g + j][16 * r + n] = z[j];
+                for (int j = 0; j < 4; ++j) sm.part[w][4 * g + j][16 * r + n] = z[j] + b2v;
             }
         }
         // step of W2 (W2 += t X2^T ng2), after its last use at the block start
@@ -426,9 +427,9 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
 
         // ---- P5: Zb2, out = q + LN(Zb2); stage the next mini-batch ----
         if (lnw) {
-            f32x4 z = *(const f32x4 *)&sm.b2[4 * n];
+            f32x4 z = *(const f32x4 *)&sm.part[0][t][4 * n];  // includes b2
 #pragma unroll
-            for (int p = 0; p < kParts; ++p) z += *(const f32x4 *)&sm.part[p][t][4 * n];
+            for (int p = 1; p < kParts; ++p) z += *(const f32x4 *)&sm.part[p][t][4 * n];
             const f32x4 qres = *(const f32x4 *)&sm.qres[buf][t][4 * n];
             float s1 = (z[0] + z[1]) + (z[2] + z[3]);
             float s2 = fmaf(z[0], z[0], z[1] * z[1]) + fmaf(z[2], z[2], z[3] * z[3]);
@@ -451,7 +452,9 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
                 }
             }
         }
-        phase_barrier();  // part, x2, xb2, ng2 free
+        // no barrier here: the LayerNorm waves' P5 overlaps the other waves' P0
+        // of the next block, which writes none of what P5 reads (part is next
+        // written in P1, behind B1; b2 rides in slice 0 of part)
     }
 
     // ---- final state (an open last mini-batch left W, b at its start) ----

@@ -391,7 +391,10 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
                 if (g == 0) sm.b2n[16 * r + n] = bn[0];
             }
         }
-        phase_barrier();  // B4: Xb2 in LDS
+        // P4 reads only this wave's own columns of Xb2 (and of X2), written by
+        // this wave above: a wave's LDS accesses run in order, so no barrier,
+        // only a fence that keeps the compiler from hoisting the reads
+        wave_lds_order();
 
         // ---- P4: partial Zb2 over this hidden slice, with this slice's part
         // of the causal term: tril(Xb2 X2^T + 1) ng2 is the sum over the

@@ -59,7 +59,7 @@ struct Smem {
     _Float16 x2[kM][HP];      // X2 = GELU(Z1), [token][hidden]
     _Float16 xb2[kM][HP];     // Xb2 = GELU(Zb1)
     _Float16 ng2[kM][NP];     // ng2, [token][d]
-    float part[kParts][kM][FP];  // partial sums of Z2 / Zb2, [slice][token][d]
+    float part[2][kParts][kM][FP];  // partial sums [slice][token][d]: [0] of Z2, [1] of Zb2
     float cel[2][kM][kD];     // eta (gamma (k - v) + gamma beta), by mini-batch parity
     float qres[2][kM][kD];    // q + beta (the residual of the output), by parity
     float eta[2][kM];         // learning rate per token, by parity
@@ -291,7 +291,10 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
             M1 = to_h4(m);
         }
         if (nb > 0 && threadIdx.x < kD) sm.b2[threadIdx.x] = sm.b2n[threadIdx.x];  // previous step
-        phase_barrier();  // B1: X2 in LDS, b2 current
+        // P1 reads only this wave's own columns of X2, written above: a
+        // wave-local fence, no barrier (P1 writes the Z2 partials, which only
+        // P2 reads, behind B2; the previous block's P5 reads the Zb2 partials)
+        wave_lds_order();
 
         // ---- P1: partial Z2 over this hidden slice ----
         const h8 x2p = row_perm(&sm.x2[0][0], HP, n, g, 32 * w);
@@ -299,7 +302,7 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
         for (int r = 0; r < 4; ++r) {
             const f32x4 z2 = mfma32(x2p, pair_b(W2s[0][r], W2s[1][r]), zero);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sm.part[w][4 * g + j][16 * r + n] = z2[j];
+            for (int j = 0; j < 4; ++j) sm.part[0][w][4 * g + j][16 * r + n] = z2[j];
         }
         phase_barrier();  // B2
 
@@ -307,7 +310,7 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
         if (lnw) {
             f32x4 z = *(const f32x4 *)&sm.b2[4 * n];
 #pragma unroll
-            for (int p = 0; p < 8; ++p) z += *(const f32x4 *)&sm.part[p][t][4 * n];
+            for (int p = 0; p < 8; ++p) z += *(const f32x4 *)&sm.part[0][p][t][4 * n];
             const f32x4 cel = *(const f32x4 *)&sm.cel[buf][t][4 * n];
             const float eta = sm.eta[buf][t];
             // mean and mean square in one reduction round
@@ -412,7 +415,7 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
                 const f32x4 z = mfma16(M2, G2[r], mfma32(xb2p, pair_b(W2s[0][r], W2s[1][r]), zero));
                 const float b2v = w == 0 ? sm.b2[16 * r + n] : 0.f;  // b2 (current) rides in slice 0
 #pragma unroll
-                for (int j = 0; j < 4; ++j) sm.part[w][4 * g + j][16 * r + n] = z[j] + b2v;
+                for (int j = 0; j < 4; ++j) sm.part[1][w][4 * g + j][16 * r + n] = z[j] + b2v;
             }
         }
         // step of W2 (W2 += t X2^T ng2), after its last use at the block start
@@ -430,9 +433,9 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
 
         // ---- P5: Zb2, out = q + LN(Zb2); stage the next mini-batch ----
         if (lnw) {
-            f32x4 z = *(const f32x4 *)&sm.part[0][t][4 * n];  // includes b2
+            f32x4 z = *(const f32x4 *)&sm.part[1][0][t][4 * n];  // includes b2
 #pragma unroll
-            for (int p = 1; p < kParts; ++p) z += *(const f32x4 *)&sm.part[p][t][4 * n];
+            for (int p = 1; p < kParts; ++p) z += *(const f32x4 *)&sm.part[1][p][t][4 * n];
             const f32x4 qres = *(const f32x4 *)&sm.qres[buf][t][4 * n];
             float s1 = (z[0] + z[1]) + (z[2] + z[3]);
             float s2 = fmaf(z[0], z[0], z[1] * z[1]) + fmaf(z[2], z[2], z[3] * z[3]);
@@ -456,8 +459,8 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
             }
         }
         // no barrier here: the LayerNorm waves' P5 overlaps the other waves' P0
-        // of the next block, which writes none of what P5 reads (part is next
-        // written in P1, behind B1; b2 rides in slice 0 of part)
+        // and P1 of the next block, which write none of what P5 reads (the Zb2
+        // partials are next written in P4, behind B2; b2 rides in slice 0)
     }
 
     // ---- final state (an open last mini-batch left W, b at its start) ----

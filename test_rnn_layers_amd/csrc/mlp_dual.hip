@@ -42,7 +42,7 @@ namespace {
 constexpr int kM = 16;
 constexpr int kF = 256;
 constexpr int XP = 72;    // f16 row pitch of the 16x64 tiles
-constexpr int HP = 264;   // f16 row pitch of the 16x256 tiles
+constexpr int HP = 268;   // f16 row pitch of the 16x256 tiles (134 dwords: the column writes of X2, Xb2 hit 32 distinct banks)
 constexpr int NP = 68;    // f16 row pitch of the ng2 tile
 constexpr int FP = 68;    // fp32 row pitch of the partial sums
 constexpr int kParts = 8; // hidden slices

@@ -339,8 +339,8 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) sm.ng2T[4 * n + e][t] = ngh[e];
         } else if (nb + 1 < NB) {
-            // stage the next mini-batch (its buffers were last read in P0 of nb-1
-            // and P5 of nb-1)
+            // stage the next mini-batch (its buffers were last read in P0, P2, P3
+            // and P5 of nb-1, all before B2 of this block)
             stage(pre, buf ^ 1);
             if (nb + 2 < NB) fetch(pre, nb + 2);
         }
@@ -431,7 +431,7 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
         }
         phase_barrier();  // B5
 
-        // ---- P5: Zb2, out = q + LN(Zb2); stage the next mini-batch ----
+        // ---- P5 (LayerNorm waves): Zb2, out = q + LN(Zb2) ----
         if (lnw) {
             f32x4 z = *(const f32x4 *)&sm.part[1][0][t][4 * n];  // includes b2
 #pragma unroll

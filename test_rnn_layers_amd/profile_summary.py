@@ -17,6 +17,7 @@ known byte count to what the same counter read for the copy.
 from __future__ import annotations
 
 import argparse
+import collections
 import csv
 import glob
 import hashlib
@@ -118,6 +119,44 @@ def traffic_summary(fetch_dir, write_dir, kernel, workload, copy_mb, cmd):
     return "\n".join(lines) + "\n"
 
 
+def sq_summary(dirs, kernel, cmd, blocks_per_chain):
+    """Shader-sequencer counters of one kernel (SQ_*), summed over its
+    dispatches and divided by the dispatch count, with per-wave figures.
+    SQ_WAVE_CYCLES, SQ_BUSY_CYCLES and the SQ_ACTIVE_* / SQ_WAIT_* counters
+    count in units of four cycles."""
+    vals = collections.defaultdict(list)
+    for d in dirs:
+        for f in _find(d, "counter_collection.csv"):
+            for r in csv.DictReader(open(f)):
+                if kernel in r["Kernel_Name"]:
+                    vals[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {kernel} dispatches with SQ counters")
+    m = {k: statistics.mean(v) for k, v in vals.items()}
+    lines = [f"# Shader-sequencer counters of {kernel}", "", "Commands:", "", "```", cmd, "```", "",
+             "| counter | mean per dispatch | dispatches |", "|---|---|---|"]
+    for k in sorted(m):
+        lines.append(f"| {k} | {m[k]:.4g} | {len(vals[k])} |")
+    waves = m.get("SQ_WAVES", 0)
+    if waves and "SQ_WAVE_CYCLES" in m:
+        wc = m["SQ_WAVE_CYCLES"] / waves
+        lines += ["", f"Per wave ({waves:.0f} waves per dispatch, {wc * 4:.0f} cycles each):"]
+        if "SQ_INSTS_VALU" in m:
+            per = m["SQ_INSTS_VALU"] / waves
+            lines.append(f"- VALU instructions: {per:.0f}" + (
+                f" ({per / blocks_per_chain:.0f} per mini-batch)" if blocks_per_chain else ""))
+        for name in ("SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_ANY", "SQ_WAIT_INST_LDS",
+                     "SQ_LDS_BANK_CONFLICT"):
+            if name in m:
+                lines.append(f"- {name}: {m[name] / waves / wc:.1%} of the wave's cycles (counter / waves / "
+                             f"SQ_WAVE_CYCLES per wave)")
+        if "SQ_LDS_BANK_CONFLICT" in m and m.get("SQ_ACTIVE_INST_LDS"):
+            lines.append(f"- SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS = "
+                         f"{m['SQ_LDS_BANK_CONFLICT'] / m['SQ_ACTIVE_INST_LDS']:.2f}")
+    lines.append(f"- kernel source sha256 {source_digest(kernel)[:16]}...")
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -134,9 +173,17 @@ def main():
     t.add_argument("--copy-mb", type=int, required=True)
     t.add_argument("--cmd", required=True)
     t.add_argument("--out", required=True)
+    q = sub.add_parser("sq")
+    q.add_argument("dirs", nargs="+")
+    q.add_argument("--kernel", required=True)
+    q.add_argument("--blocks-per-chain", type=int, default=0, help="mini-batches per chain (per-mini-batch figures)")
+    q.add_argument("--cmd", required=True)
+    q.add_argument("--out", required=True)
     a = ap.parse_args()
     if a.cmd_name == "stats":
         text = stats_summary(a.dir, a.kernel, a.cmd)
+    elif a.cmd_name == "sq":
+        text = sq_summary(a.dirs, a.kernel, a.cmd, a.blocks_per_chain)
     else:
         text = traffic_summary(a.fetch, a.write, a.kernel, a.workload, a.copy_mb, a.cmd)
     os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)

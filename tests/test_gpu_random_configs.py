@@ -50,3 +50,15 @@ def test_mlp_random_configuration(i, c):
     _run(f"random_mlp_{i}_{c}", inp, rope=c["rope"], pieces=tuple(c["cuts"]), out_dtype=c["out_dtype"],
          token_eta=c["te"], K=c["K"], in_dtype=c["dtype"], decode=c["decode"],
          tol=TOL_F32 if c["dtype"] == "f32" else TOL_BF16, grad_layout=c["layout"])
+
+
+def test_linear_more_chains_than_cus():
+    """288 chains: more workgroups than the chip has CUs, two per CU at a time."""
+    inp = make_inputs(6, 48, 40, dtype="bf16", seed=3001, rich=True)
+    _check_full("linear_288_chains", inp, dtype="bf16", pieces=[9], decode={9})
+
+
+def test_mlp_more_chains_than_cus():
+    """280 chains of TTT-MLP (one workgroup per CU, in several waves of dispatch)."""
+    inp = make_inputs(5, 56, 36, dtype="bf16", seed=3002, rich=True, mlp_hidden=256)
+    _run("mlp_280_chains", inp, pieces=(16,))

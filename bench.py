@@ -614,7 +614,7 @@ def bench_mlp_decode(args, w):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the (batch, head) "
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); the (batch, head) "
               "chains are independent, so more GPUs would each take a share of the batch", file=sys.stderr)
         sys.exit(2)
     from test_rnn_layers_amd.synth import WORKLOADS

@@ -105,3 +105,50 @@ def test_binding_cfg_layouts():
     d = libttt.eta_desc(torch.ones(2, 3, 40))
     assert (d.sB, d.sH) == (120, 40)
     np.testing.assert_equal(libttt.STATUS_NAMES[7], "TTT_ERR_UNSUPPORTED")
+
+
+def _counter_csv(path, rows):
+    import csv
+
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Dispatch_Id", "Grid_Size", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for r in rows:
+            w.writerow(r)
+
+
+def test_profile_traffic_scaling(tmp_path, monkeypatch):
+    """FETCH_SIZE / WRITE_SIZE of a kernel scaled by what they read for the copy probe."""
+    from test_rnn_layers_amd import profile_summary as ps
+
+    monkeypatch.setattr(ps, "TRAFFIC_JSON", str(tmp_path / "traffic.json"))
+    mb = 64
+    _counter_csv(str(tmp_path / "f" / "p_counter_collection.csv"),
+                 [(1, 512, "linear_dual_kernel", "FETCH_SIZE", 1000.0), (2, 512, "linear_dual_kernel", "FETCH_SIZE", 1000.0),
+                  (3, 4096, "__amd_rocclr_copyBuffer", "FETCH_SIZE", mb * 512.0),
+                  (4, 4096, "__amd_rocclr_copyBuffer", "FETCH_SIZE", mb * 512.0)])
+    _counter_csv(str(tmp_path / "w" / "p_counter_collection.csv"),
+                 [(1, 512, "linear_dual_kernel", "WRITE_SIZE", 300.0),
+                  (3, 4096, "__amd_rocclr_copyBuffer", "WRITE_SIZE", mb * 1024.0),
+                  (4, 4096, "__amd_rocclr_copyBuffer", "WRITE_SIZE", mb * 1024.0)])
+    ps.traffic_summary(str(tmp_path / "f"), str(tmp_path / "w"), "linear_dual_kernel", "wl", mb, "cmd")
+    import json
+
+    rec = json.load(open(tmp_path / "traffic.json"))["linear_dual_kernel@wl"]
+    assert rec["fetch_scale"] == pytest.approx(2.0) and rec["write_scale"] == pytest.approx(1.0)
+    assert rec["hbm_bytes_per_launch"] == pytest.approx(1000 * 1024 * 2 + 300 * 1024)
+
+
+def test_profile_sq_per_wave(tmp_path):
+    """Per-wave figures of the shader-sequencer summary (cycle counters in units of 4 cycles)."""
+    from test_rnn_layers_amd import profile_summary as ps
+
+    rows = [(1, 512, "mlp_dual_kernel", "SQ_WAVES", 8.0), (1, 512, "mlp_dual_kernel", "SQ_WAVE_CYCLES", 8000.0),
+            (1, 512, "mlp_dual_kernel", "SQ_INSTS_VALU", 1600.0), (1, 512, "mlp_dual_kernel", "SQ_ACTIVE_INST_VALU", 2000.0),
+            (1, 512, "other_kernel", "SQ_INSTS_VALU", 1e9)]
+    _counter_csv(str(tmp_path / "p" / "p_counter_collection.csv"), rows)
+    text = ps.sq_summary([str(tmp_path / "p")], "mlp_dual_kernel", "cmd", 2)
+    assert "8 waves per dispatch, 4000 cycles each" in text
+    assert "VALU instructions: 200 (100 per mini-batch)" in text
+    assert "SQ_ACTIVE_INST_VALU: 25.0% of the wave's cycles" in text

@@ -185,6 +185,19 @@ def test_bf16_output():
     _check_full("bf16_out", inp, dtype="bf16", out_dtype="bf16")
 
 
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rope", [False, True])
+@pytest.mark.parametrize("te", [False, True])
+def test_every_dual_instantiation(in_dtype, out_dtype, rope, te):
+    """Each of the 16 compiled variants of the dual kernel (input dtype,
+    output dtype, rotary, token_eta) once, on a ragged length."""
+    token_eta = (0.5 + np.arange(16) / 16.0).tolist() if te else None
+    inp = make_inputs(2, 3, 16 * 5 + 3, dtype=in_dtype, seed=61 + 2 * rope + te, rich=True)
+    _check_full(f"dual_{in_dtype}_{out_dtype}_rope{int(rope)}_te{int(te)}", inp, dtype=in_dtype, rope=rope,
+                out_dtype=out_dtype, token_eta=token_eta)
+
+
 def test_deterministic():
     inp = make_inputs(2, 4, 96, dtype="bf16", seed=9, rich=True)
     outs = []

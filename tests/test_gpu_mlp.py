@@ -142,6 +142,17 @@ def test_bf16_output():
     _run("mlp_bf16_out", inp, out_dtype="bf16")
 
 
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rope", [False, True])
+@pytest.mark.parametrize("te", [False, True])
+def test_every_dual_instantiation(out_dtype, rope, te):
+    """Each compiled variant of the dual-form MLP kernel (output dtype,
+    rotary), with and without token_eta, on a ragged length."""
+    token_eta = (0.5 + np.arange(16) / 16.0).tolist() if te else None
+    inp = make_inputs(2, 2, 16 * 4 + 5, dtype="bf16", seed=71 + 2 * rope + te, rich=True, mlp_hidden=256)
+    _run(f"mlp_dual_{out_dtype}_rope{int(rope)}_te{int(te)}", inp, rope=rope, out_dtype=out_dtype, token_eta=token_eta)
+
+
 def test_eta_zero_is_frozen_mlp():
     """With eta = 0 the fast weights never move: out = Q + LN(f(Q)) with the
     initial f, and the state keeps its initial values."""

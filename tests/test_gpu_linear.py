@@ -198,6 +198,18 @@ def test_every_dual_instantiation(in_dtype, out_dtype, rope, te):
                 out_dtype=out_dtype, token_eta=token_eta)
 
 
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("layout", ["dense", "rows"])
+def test_every_token_instantiation(in_dtype, out_dtype, layout):
+    """Each compiled variant of the token kernel (input and output dtype,
+    gradient layout): a prefill piece, then decode calls across a commit."""
+    inp = make_inputs(2, 2, 40, dtype=in_dtype, seed=81, rich=True)
+    cuts = [21, 29, 30, 33]
+    _check_full(f"token_{in_dtype}_{out_dtype}_{layout}", inp, dtype=in_dtype, out_dtype=out_dtype, pieces=cuts,
+                decode=set(cuts), grad_layout=layout, rope=True)
+
+
 def test_deterministic():
     inp = make_inputs(2, 4, 96, dtype="bf16", seed=9, rich=True)
     outs = []

@@ -153,6 +153,19 @@ def test_every_dual_instantiation(out_dtype, rope, te):
     _run(f"mlp_dual_{out_dtype}_rope{int(rope)}_te{int(te)}", inp, rope=rope, out_dtype=out_dtype, token_eta=token_eta)
 
 
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("layout", ["dense", "rows"])
+def test_every_token_instantiation(in_dtype, out_dtype, layout):
+    """Each compiled variant of the MLP token kernel (input and output dtype,
+    gradient layout): a prefill piece, then decode calls across a commit."""
+    inp = make_inputs(1, 2, 40, dtype=in_dtype, seed=91, rich=True, mlp_hidden=256)
+    cuts = (21, 29, 30, 33)
+    _run(f"mlp_token_{in_dtype}_{out_dtype}_{layout}", inp, pieces=cuts, decode=set(cuts), out_dtype=out_dtype,
+         in_dtype=in_dtype, tol=1e-4 if in_dtype == "f32" and out_dtype == "f32" else TOL_BF16, grad_layout=layout,
+         rope=True)
+
+
 def test_eta_zero_is_frozen_mlp():
     """With eta = 0 the fast weights never move: out = Q + LN(f(Q)) with the
     initial f, and the state keeps its initial values."""

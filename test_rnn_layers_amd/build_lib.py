@@ -65,9 +65,25 @@ def build(asm: bool = False, verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    _build_c_example()
     if verbose:
-        print(f"built {LIB} from {', '.join(srcs)}")
+        print(f"built {LIB} from {', '.join(srcs)}; {C_EXAMPLE}")
     return LIB
+
+
+C_EXAMPLE = os.path.join(os.path.dirname(LIB), "ttt_c_example")
+
+
+def _build_c_example() -> None:
+    """A plain-C program that uses the library through include/ttt.h only."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(_hipcc())))
+    cmd = [os.environ.get("CC", "gcc"), "-O2", "-std=c11", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE,
+           "-I", os.path.join(rocm, "include"), os.path.join(CSRC, "c_example.c"), "-o", C_EXAMPLE,
+           "-L", os.path.dirname(LIB), "-lttt", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"C example build failed\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
 
 
 if __name__ == "__main__":

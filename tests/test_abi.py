@@ -203,3 +203,15 @@ def test_mlp_state_init_errors():
     assert T.STATUS_NAMES[lib.ttt_mlp_state_init(ctypes.byref(_mlp_cfg(F=64)), _addr(1), _addr(2), _addr(3),
                                                  _addr(4), ctypes.byref(st), None)] == "TTT_ERR_SHAPE"
     assert st.offset == 7
+
+
+def test_c_example_is_built_against_the_header():
+    """The plain-C example links libttt and imports the entry points it uses
+    from it (it is run, against the oracle, by a GPU test)."""
+    import subprocess
+    from test_rnn_layers_amd.build_lib import C_EXAMPLE
+
+    assert os.path.exists(C_EXAMPLE)
+    und = subprocess.run(["nm", "-D", "--undefined-only", C_EXAMPLE], capture_output=True, text=True).stdout
+    for sym in ("ttt_linear_state_init", "ttt_linear_prefill", "ttt_linear_decode", "ttt_last_error"):
+        assert sym in und, sym

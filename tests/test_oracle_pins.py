@@ -491,3 +491,117 @@ def test_mlp_eta_zero_closed_form(orc):
     ref = q + Fn.layer_norm(T(h), (D,), T(gam), T(bet), EPS).numpy()
     np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
     assert math.isclose(np.abs(st[0] - W1).max(), 0.0)
+
+
+# ----------------------------------------------------------------------------
+# Batch drivers (the all-chain checkers of the full-size GPU tests): each
+# chain against the autograd definition, with learning rates that differ per
+# batch row ([B, H, L], as "代码连连看——TTT" compute_mini_batch takes eta per
+# batch and head), distinct per-chain start states and F != D, so that a
+# wrong batch, head or state stride shows in some chain.
+# ----------------------------------------------------------------------------
+def _per_batch_eta(r, B, H, L):
+    return 1 / (1 + np.exp(-r.normal(size=(B, H, L)))) / 8
+
+
+@pytest.mark.parametrize("eta_per_batch", [False, True])
+def test_linear_batch_driver_matches_definition(orc, eta_per_batch):
+    B, H, L, D, K = 2, 3, 12, 8, 4
+    r = _rng(301 + eta_per_batch)
+    XQ, XK, XV = (r.normal(size=(B, H, L, D)) for _ in range(3))
+    eta = _per_batch_eta(r, B, H, L) if eta_per_batch else _per_batch_eta(r, 1, H, L)[0]
+    lw, lb = 1 + 0.2 * r.normal(size=(H, D)), 0.2 * r.normal(size=(H, D))
+    W = r.normal(size=(B, H, D, D)) * 0.1  # every chain its own start state
+    b = 0.05 * r.normal(size=(B, H, D))
+    W0, b0 = W.copy(), b.copy()
+    G, gb = np.zeros_like(W), np.zeros_like(b)
+    out = orc.linear_batch(XQ, XK, XV, eta, H * L if eta_per_batch else 0, lw, lb, W, b, G, gb, K=K, rope=True)
+    for bi in range(B):
+        for h in range(H):
+            e = eta[bi, h] if eta_per_batch else eta[h]
+            ref, Wr, br = _linear_by_autograd(XQ[bi, h], XK[bi, h], XV[bi, h], e, lw[h], lb[h], W0[bi, h],
+                                              b0[bi, h], K=K, rope=True)
+            np.testing.assert_allclose(out[bi, h], ref, rtol=1e-10, atol=1e-10)
+            np.testing.assert_allclose(W[bi, h], Wr, rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(b[bi, h], br, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("eta_per_batch", [False, True])
+def test_mlp_batch_driver_matches_definition(orc, eta_per_batch):
+    B, H, L, D, F, K = 2, 2, 8, 8, 16, 4
+    r = _rng(311 + eta_per_batch)
+    XQ, XK, XV = (r.normal(size=(B, H, L, D)) for _ in range(3))
+    eta = _per_batch_eta(r, B, H, L) if eta_per_batch else _per_batch_eta(r, 1, H, L)[0]
+    lw, lb = 1 + 0.2 * r.normal(size=(H, D)), 0.2 * r.normal(size=(H, D))
+    W1, W2 = r.normal(size=(B, H, D, F)) * 0.2, r.normal(size=(B, H, F, D)) * 0.2
+    b1, b2 = 0.05 * r.normal(size=(B, H, F)), 0.05 * r.normal(size=(B, H, D))
+    init = [a.copy() for a in (W1, b1, W2, b2)]
+    G = [np.zeros_like(W1), np.zeros_like(b1), np.zeros_like(W2), np.zeros_like(b2)]
+    out = orc.mlp_batch(XQ, XK, XV, eta, H * L if eta_per_batch else 0, lw, lb, W1, b1, W2, b2, *G, K=K)
+    for bi in range(B):
+        for h in range(H):
+            e = eta[bi, h] if eta_per_batch else eta[h]
+            ref, Pr = _mlp_by_autograd(XQ[bi, h], XK[bi, h], XV[bi, h], e, lw[h], lb[h],
+                                       *[a[bi, h] for a in init], K=K)
+            np.testing.assert_allclose(out[bi, h], ref, rtol=1e-9, atol=1e-10)
+            for got, want in zip((W1, b1, W2, b2), Pr):
+                np.testing.assert_allclose(got[bi, h], want, rtol=1e-9, atol=1e-12)
+
+
+def test_batch_drivers_open_state_and_offset(orc):
+    """Batch drivers started mid-mini-batch from a carried open state equal
+    the per-chain routine (itself pinned by split invariance above) chain by
+    chain, for both layers, with per-batch learning rates and token_eta."""
+    B, H, D, F, K, P, L = 2, 2, 8, 16, 4, 6, 9
+    r = _rng(321)
+    XQ, XK, XV = (r.normal(size=(B, H, P + L, D)) for _ in range(3))
+    eta = _per_batch_eta(r, B, H, P + L)
+    lw, lb = 1 + 0.2 * r.normal(size=(H, D)), 0.2 * r.normal(size=(H, D))
+    te = _token_eta(K, 3)
+    # TTT-Linear: carry P tokens per chain, then the batch driver from offset P
+    W, b = r.normal(size=(B, H, D, D)) * 0.1, 0.05 * r.normal(size=(B, H, D))
+    G, gb = np.zeros_like(W), np.zeros_like(b)
+    ref_out = np.empty((B, H, L, D))
+    ref_state = [np.empty_like(a) for a in (W, b, G, gb)]
+    for bi in range(B):
+        for h in range(H):
+            s = [W[bi, h].copy(), b[bi, h].copy(), G[bi, h].copy(), gb[bi, h].copy()]
+            orc.linear_chain(XQ[bi, h, :P], XK[bi, h, :P], XV[bi, h, :P], eta[bi, h, :P], lw[h], lb[h], *s, K=K,
+                             token_eta=te)
+            for a, x in zip((W, b, G, gb), s):
+                a[bi, h] = x
+            t = [x.copy() for x in s]
+            ref_out[bi, h] = orc.linear_chain(XQ[bi, h, P:], XK[bi, h, P:], XV[bi, h, P:], eta[bi, h, P:], lw[h],
+                                              lb[h], *t, K=K, offset=P, token_eta=te)
+            for a, x in zip(ref_state, t):
+                a[bi, h] = x
+    assert np.abs(G).max() > 0  # the carried state is open
+    out = orc.linear_batch(XQ[:, :, P:], XK[:, :, P:], XV[:, :, P:], np.ascontiguousarray(eta[:, :, P:]), H * L,
+                           lw, lb, W, b, G, gb, K=K, offset=P, token_eta=te)
+    np.testing.assert_array_equal(out, ref_out)
+    for a, x in zip((W, b, G, gb), ref_state):
+        np.testing.assert_array_equal(a, x)
+    # TTT-MLP, the same
+    st = [r.normal(size=(B, H, D, F)) * 0.2, 0.05 * r.normal(size=(B, H, F)), r.normal(size=(B, H, F, D)) * 0.2,
+          0.05 * r.normal(size=(B, H, D)), np.zeros((B, H, D, F)), np.zeros((B, H, F)), np.zeros((B, H, F, D)),
+          np.zeros((B, H, D))]
+    ref_out = np.empty((B, H, L, D))
+    ref_state = [np.empty_like(a) for a in st]
+    for bi in range(B):
+        for h in range(H):
+            s = [a[bi, h].copy() for a in st]
+            orc.mlp_chain(XQ[bi, h, :P], XK[bi, h, :P], XV[bi, h, :P], eta[bi, h, :P], lw[h], lb[h], *s, K=K,
+                          token_eta=te)
+            for a, x in zip(st, s):
+                a[bi, h] = x
+            t = [x.copy() for x in s]
+            ref_out[bi, h] = orc.mlp_chain(XQ[bi, h, P:], XK[bi, h, P:], XV[bi, h, P:], eta[bi, h, P:], lw[h],
+                                           lb[h], *t, K=K, offset=P, token_eta=te)
+            for a, x in zip(ref_state, t):
+                a[bi, h] = x
+    assert np.abs(st[4]).max() > 0 and np.abs(st[6]).max() > 0
+    out = orc.mlp_batch(XQ[:, :, P:], XK[:, :, P:], XV[:, :, P:], np.ascontiguousarray(eta[:, :, P:]), H * L, lw,
+                        lb, *st, K=K, offset=P, token_eta=te)
+    np.testing.assert_array_equal(out, ref_out)
+    for a, x in zip(st, ref_state):
+        np.testing.assert_array_equal(a, x)

@@ -57,9 +57,31 @@
  *    sL = D.  Data pointers and every stride in bytes must be multiples of
  *    16 bytes.
  *  - Errors: on any status other than TTT_OK nothing has been enqueued and
- *    the state (including ``offset``) is unchanged.  ttt_last_error()
- *    returns a per-thread message describing the last failure.
+ *    the state (including ``offset``) is unchanged, with one exception: a
+ *    call is split into up to three launches (below), and if the runtime
+ *    refuses a later launch after an earlier one was enqueued, the call
+ *    returns TTT_ERR_HIP with ``offset`` advanced by the tokens of the
+ *    enqueued launches (their work completes; the state is consistent with
+ *    the new offset).  An error left by an earlier HIP call on the thread is
+ *    reported (and cleared) as TTT_ERR_HIP before anything is enqueued.
+ *    ttt_last_error() returns a per-thread message describing the last
+ *    failure.
+ *  - Inputs (XQ, XK, XV, eta, ln_w, ln_b, token_eta) and out must not
+ *    overlap the state buffers, and out must not overlap an input
+ *    (TTT_ERR_ALIAS).
  *  - NaN/Inf in the inputs propagate to the outputs; they are not checked.
+ *  - Range of bf16 inputs.  With bf16 inputs, whole mini-batches (K = 16) run
+ *    their products on fp16 MFMA operands with fp32 accumulation (fp16's 11
+ *    significant bits keep the 2e-2 output bar that bf16's 8 would not).
+ *    The gradients are carried scaled by 2^8 and the 16x16 matrices they
+ *    multiply by 2^-8, which leaves every product unchanged; the values must
+ *    then stay within fp16's range: |q|, |k| (after rotary) and |W| (TTT-MLP:
+ *    |W1|, |W2|, |GELU(x W1 + b1)|) at most 65504; dot products of two
+ *    q/k rows of a mini-batch, of k rows of neighbouring mini-batches and
+ *    (TTT-MLP) of two hidden-activation rows below 2^8 * 65504 = 1.7e7; and
+ *    |eta_j g_j| elementwise below 256.  Outside these bounds the results
+ *    are undefined (typically inf or NaN).  fp32 inputs have no such bounds
+ *    (fp32 MFMA for TTT-Linear, fp32 arithmetic for TTT-MLP).
  *  - Calls on one state must be ordered (same stream, or synchronised);
  *    calls on distinct states and buffers may run concurrently.
  */
@@ -78,7 +100,7 @@ typedef enum ttt_status {
     TTT_ERR_SHAPE = 2,       /* D != 64, K outside 1..16, B/H/L < 1, F != 256 */
     TTT_ERR_DTYPE = 3,       /* unknown in/out dtype */
     TTT_ERR_ALIGN = 4,       /* pointer or stride not a multiple of 16 bytes */
-    TTT_ERR_ALIAS = 5,       /* out overlaps an input or the state */
+    TTT_ERR_ALIAS = 5,       /* out overlaps an input or the state, or an input overlaps the state */
     TTT_ERR_STATE = 6,       /* negative offset, or state incompatible with the call */
     TTT_ERR_UNSUPPORTED = 7, /* valid request outside what is implemented */
     TTT_ERR_HIP = 8          /* the HIP runtime reported an error at launch */

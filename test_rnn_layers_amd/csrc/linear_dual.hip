@@ -32,6 +32,12 @@
 //  * Operands: bf16 inputs run the products on fp16 MFMA (inputs, W, ng and
 //    the 16x16 matrices rounded to fp16; fp32 accumulation); fp32 inputs run
 //    them on fp32 MFMA.
+//  * Range: ng is carried as 2^8 ng and the 16x16 matrices (and the K^T and
+//    ones operands of the state step) as 2^-8 of their values, so every
+//    product is unchanged (powers of two are exact) while dot products of q
+//    and k up to 2^8 * 65504 = 1.7e7 stay inside fp16, and ng values down to
+//    2^-22 stay normal.  What fp16 still bounds: |q|, |k|, |W| <= 65504 and
+//    |eta g| < 256 elementwise.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -43,6 +49,9 @@ namespace {
 constexpr int kM = 16;     // mini-batch size of this kernel
 constexpr int kRing = 4;   // LDS stages and register sets (mini-batch mod 4)
 constexpr int kFP = 68;    // fp32 row pitch of the exchange buffers
+// ng is carried scaled by kNgScale, the matrices that multiply it by 1/kNgScale
+constexpr float kNgScale = 256.f;
+constexpr float kMatScale = 1.f / kNgScale;
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -384,7 +393,7 @@ struct RowWave {
         float su = (u[0] + u[1]) + (u[2] + u[3]);
         float sux = fmaf(u[0], xh[0], u[1] * xh[1]) + fmaf(u[2], xh[2], u[3] * xh[3]);
         row_sum16x2(su, sux);
-        const float A = -rr.eta * rs;
+        const float A = -kNgScale * rr.eta * rs;  // 2^8 ng
         const float C0 = -A * su * (1.f / kD), C1 = -A * sux * (1.f / kD);
         float ng[4];
 #pragma unroll
@@ -574,9 +583,10 @@ __device__ void col_main(const LinearArgs &a, Smem<T> &sm, int ch, int c, int g,
         const float bv = a.b[(int64_t)ch * kD + 16 * c + n];
         Bt = f32x4{bv, bv, bv, bv};
     }
-    // token_eta of query row n, and of the last row (the carried step)
-    const float tn = TE ? a.te[n] : 1.f;
-    const float tl = TE ? a.te[kM - 1] : 1.f;
+    // token_eta of query row n, and of the last row (the carried step), both
+    // times 2^-8: the matrices and operands they scale multiply 2^8 ng
+    const float tn = (TE ? a.te[n] : 1.f) * kMatScale;
+    const float tl = (TE ? a.te[kM - 1] : 1.f) * kMatScale;
     const typename O::Sel sel = O::sel(n, g, tl);
     const F4 ones = O::make(f32x4{tl, tl, tl, tl});
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f}, one = {1.f, 1.f, 1.f, 1.f};

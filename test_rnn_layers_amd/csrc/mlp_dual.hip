@@ -29,7 +29,13 @@
 //  * waves 4..7 stage the next mini-batch while waves 0..3 run the LayerNorm
 //    backward: rotated q, k as fp16 rows and a transposed copy of k (the K^T
 //    fragments of the W1 step), and the LayerNorm operands in fp32;
-//  * operands are fp16 (bf16 inputs), accumulation fp32; GELU in the erf form.
+//  * operands are fp16 (bf16 inputs), accumulation fp32; GELU in the erf form;
+//  * range: ng2 (hence ng1) is carried as 2^8 of its value and the operands
+//    it multiplies (the causal matrices, K^T, X2, the ones of the bias steps)
+//    as 2^-8 of theirs: the products are unchanged (powers of two are exact),
+//    dot products up to 2^8 * 65504 stay inside fp16 and small gradients stay
+//    normal.  fp16 still bounds |q|, |k|, |W1|, |W2|, |GELU(Z1)| <= 65504
+//    and |eta g2|, |eta g1| < 256 elementwise.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -47,6 +53,9 @@ constexpr int NP = 68;    // f16 row pitch of the ng2 tile
 constexpr int FP = 68;    // fp32 row pitch of the partial sums
 constexpr int kParts = 8; // hidden slices
 constexpr int TP = 20;    // f16 pitch of the transposed 64x16 tiles (rows 40 B apart)
+// ng2, ng1 are carried scaled by kNgScale, the operands that multiply them by 1/kNgScale
+constexpr float kNgScale = 256.f;
+constexpr float kMatScale = 1.f / kNgScale;
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -221,8 +230,10 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
         const h4 kh = h4{(_Float16)k[0], (_Float16)k[1], (_Float16)k[2], (_Float16)k[3]};
         *(h4 *)&sm.qs[buf][t][4 * n] = h4{(_Float16)q[0], (_Float16)q[1], (_Float16)q[2], (_Float16)q[3]};
         *(h4 *)&sm.xs[buf][t][4 * n] = kh;
+        // K^T multiplies 2^8 ng1 in the W1 step: kept as 2^-8 K (exact scaling)
+        const h4 khs = kh * (_Float16)kMatScale;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm.kT[buf][4 * n + e][t] = kh[e];
+        for (int e = 0; e < 4; ++e) sm.kT[buf][4 * n + e][t] = khs[e];
         const f32x4 gm = *(const f32x4 *)&sm.gam[4 * n];
         const f32x4 bt = *(const f32x4 *)&sm.bet[4 * n], gbv = *(const f32x4 *)&sm.gb[4 * n];
         f32x4 ce, qr;
@@ -246,11 +257,14 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
     float gam2r[4];  // LayerNorm waves: gamma^2 at columns 4n .. 4n+3
 #pragma unroll
     for (int e = 0; e < 4; ++e) gam2r[e] = sm.gam2[4 * n + e];
-    const h4 ones = h4{(_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f};
-    // token_eta of query row n, and of the last row (the committed step)
-    const float tn = a.te != nullptr ? a.te[n] : 1.f;
+    // the ones of the bias steps, times 2^-8 (they multiply 2^8 ng1, 2^8 ng2)
+    const h4 ones = h4{(_Float16)kMatScale, (_Float16)kMatScale, (_Float16)kMatScale, (_Float16)kMatScale};
+    // token_eta of query row n, and of the last row (the committed step);
+    // tn scales the causal matrices, which carry 2^-8
+    const float tn = (a.te != nullptr ? a.te[n] : 1.f) * kMatScale;
     const float tl = a.te != nullptr ? a.te[kM - 1] : 1.f;
-    const h4 onesl = h4{(_Float16)tl, (_Float16)tl, (_Float16)tl, (_Float16)tl};
+    const float tls = tl * kMatScale;
+    const h4 onesl = h4{(_Float16)tls, (_Float16)tls, (_Float16)tls, (_Float16)tls};
     // the 16x16 identity as a B fragment (lane: I[4g+j][n])
     h4 ident;
 #pragma unroll
@@ -334,7 +348,7 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
             sux *= (1.f / kD);
             h4 ngh;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ngh[e] = (_Float16)(-rs * (u[e] - su - xh[e] * sux));
+            for (int e = 0; e < 4; ++e) ngh[e] = (_Float16)(-kNgScale * rs * (u[e] - su - xh[e] * sux));  // 2^8 ng2
             *(h4 *)&sm.ng2[t][4 * n] = ngh;
 #pragma unroll
             for (int e = 0; e < 4; ++e) sm.ng2T[4 * n + e][t] = ngh[e];
@@ -370,7 +384,9 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
             const f32x4 zb1 = mfma16(M1, n1, P1[s]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) sm.xb2[4 * g + j][32 * w + 16 * s + n] = (_Float16)gelu(zb1[j]);
-            x2h[s] = to_h4(X2[s]);
+            // X2^T multiplies 2^8 ng2 in the W2 step: kept as 2^-8 X2
+            x2h[s] = to_h4(f32x4{X2[s][0] * kMatScale, X2[s][1] * kMatScale, X2[s][2] * kMatScale,
+                                 X2[s][3] * kMatScale});
             n1k[s] = n1;
             if (!open) {
                 // W1 += t X^T ng1, with K^T rows 16r .. 16r+15 as A fragments
@@ -423,7 +439,7 @@ __global__ __launch_bounds__(512, 1) void mlp_dual_kernel(MlpArgs a) {
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 const h4 x2t = a.te != nullptr
-                                   ? to_h4(f32x4{X2[s][0] * tl, X2[s][1] * tl, X2[s][2] * tl, X2[s][3] * tl})
+                                   ? to_h4(f32x4{X2[s][0] * tls, X2[s][1] * tls, X2[s][2] * tls, X2[s][3] * tls})
                                    : x2h[s];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) W2s[s][r] = mfma16(x2t, G2[r], W2s[s][r]);

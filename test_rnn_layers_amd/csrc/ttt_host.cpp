@@ -132,8 +132,12 @@ ttt_status check_acts(const Act &x, int B, int H, int L, int D, int K, int32_t i
                          flat_range(x.eta.token_eta, x.eta.token_eta ? K : 0, 4)};
     for (const Range &r : rin)
         if (overlap(ro, r)) return fail(TTT_ERR_ALIAS, "out overlaps an input");
-    for (const Range &r : state_ranges)
+    for (const Range &r : state_ranges) {
         if (overlap(ro, r)) return fail(TTT_ERR_ALIAS, "out overlaps the state");
+        // the kernels write the state while they read the inputs
+        for (const Range &i : rin)
+            if (overlap(i, r)) return fail(TTT_ERR_ALIAS, "an input overlaps the state");
+    }
     return TTT_OK;
 }
 
@@ -214,6 +218,25 @@ ttt_status hip_fail(hipError_t e, const char *what) {
     return fail(TTT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// A launch's error is read with hipGetLastError, which would also return an
+// error left by an earlier, unrelated HIP call on this thread.  Such an error
+// is taken (and cleared) before the first launch of a call, so the call
+// reports it with nothing enqueued.
+ttt_status take_pending_error() {
+    if (hipError_t e = hipGetLastError(); e != hipSuccess)
+        return fail(TTT_ERR_HIP, "an earlier HIP call on this thread left an error (%s); nothing was enqueued",
+                    hipGetErrorString(e));
+    return TTT_OK;
+}
+
+// A call made of several launches that fails after some of them were
+// enqueued: the state has advanced by the tokens of those pieces.
+ttt_status piece_fail(hipError_t e, const char *what, int64_t *offset, int done) {
+    *offset += done;
+    return fail(TTT_ERR_HIP, "%s: %s (the state advanced by the %d tokens already enqueued)", what,
+                hipGetErrorString(e), done);
+}
+
 enum class Mode { Prefill, Decode };
 
 ttt_status linear_call(Mode mode, const ttt_linear_cfg *cfg, int32_t L, const Act &x, ttt_linear_state *st,
@@ -240,6 +263,7 @@ ttt_status linear_call(Mode mode, const ttt_linear_cfg *cfg, int32_t L, const Ac
         tail = L - head - body * K;
     }
     LinearArgs a = linear_args(cfg, x, st);
+    if ((s = take_pending_error())) return s;
     hipError_t e;
     if (head > 0) {
         a.ntok = head;
@@ -259,17 +283,20 @@ ttt_status linear_call(Mode mode, const ttt_linear_cfg *cfg, int32_t L, const Ac
                                        (rows - 1) * x.XV.sL * (int64_t)ei, (rows - 1) * x.out.sL * (int64_t)eo}) +
                              (int64_t)cfg->D * 4;
         if (span < (int64_t)INT32_MAX) {
-            if ((e = launch_linear_dual(a, in_bf16, out_bf16, hs)) != hipSuccess) return hip_fail(e, "dual kernel");
+            if ((e = launch_linear_dual(a, in_bf16, out_bf16, hs)) != hipSuccess)
+                return piece_fail(e, "dual kernel", &st->offset, head);
         } else {
             a.ntok = body * K;  // token by token: same result, no 32-bit offsets
-            if ((e = launch_linear_token(a, in_bf16, out_bf16, hs)) != hipSuccess) return hip_fail(e, "token kernel");
+            if ((e = launch_linear_token(a, in_bf16, out_bf16, hs)) != hipSuccess)
+                return piece_fail(e, "token kernel", &st->offset, head);
         }
     }
     if (tail > 0) {
         a.ntok = tail;
         a.t0 = L - tail;
         a.pos0 = st->offset + (L - tail);
-        if ((e = launch_linear_token(a, in_bf16, out_bf16, hs)) != hipSuccess) return hip_fail(e, "token kernel");
+        if ((e = launch_linear_token(a, in_bf16, out_bf16, hs)) != hipSuccess)
+            return piece_fail(e, "token kernel", &st->offset, L - tail);
     }
     st->offset += L;
     return ok();
@@ -327,6 +354,7 @@ ttt_status mlp_call(Mode mode, const ttt_mlp_cfg *cfg, int32_t L, const Act &x, 
             body -= tail;
         }
     }
+    if ((s = take_pending_error())) return s;
     hipError_t e;
     if (head > 0) {
         a.ntok = head;
@@ -339,13 +367,15 @@ ttt_status mlp_call(Mode mode, const ttt_mlp_cfg *cfg, int32_t L, const Act &x, 
         a.tail = body % K;
         a.t0 = head;
         a.pos0 = st->offset + head;
-        if ((e = launch_mlp_dual(a, in_bf16, out_bf16, hs)) != hipSuccess) return hip_fail(e, "mlp kernel");
+        if ((e = launch_mlp_dual(a, in_bf16, out_bf16, hs)) != hipSuccess)
+            return piece_fail(e, "mlp kernel", &st->offset, head);
     }
     if (tail > 0) {
         a.ntok = tail;
         a.t0 = L - tail;
         a.pos0 = st->offset + (L - tail);
-        if ((e = launch_mlp_token(a, in_bf16, out_bf16, hs)) != hipSuccess) return hip_fail(e, "mlp token kernel");
+        if ((e = launch_mlp_token(a, in_bf16, out_bf16, hs)) != hipSuccess)
+            return piece_fail(e, "mlp token kernel", &st->offset, L - tail);
     }
     st->offset += L;
     return ok();
@@ -390,6 +420,7 @@ ttt_status ttt_linear_state_init(const ttt_linear_cfg *cfg, const float *W0, con
     t.seg[2] = TileSeg{state->W_grad, nullptr, 1, n * D * D};
     t.seg[3] = TileSeg{state->b_grad, nullptr, 1, n * D};
     t.n = 4;
+    if ((s = take_pending_error())) return s;
     if (hipError_t e = launch_tiles(t, hs); e != hipSuccess) return hip_fail(e, "state init");
     state->offset = 0;
     return ok();
@@ -426,6 +457,7 @@ ttt_status ttt_mlp_state_init(const ttt_mlp_cfg *cfg, const float *W1, const flo
     t.seg[6] = TileSeg{state->W2_grad, nullptr, 1, n * F * D};
     t.seg[7] = TileSeg{state->b2_grad, nullptr, 1, n * D};
     t.n = 8;
+    if ((s = take_pending_error())) return s;
     if (hipError_t e = launch_tiles(t, hs); e != hipSuccess) return hip_fail(e, "state init");
     state->offset = 0;
     return ok();

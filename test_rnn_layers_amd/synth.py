@@ -10,8 +10,11 @@ heads x 64 for the 125m style, 1024 = 16 x 64 for 350m, 2048 = 32 x 64 for the
   * one ``torch.Generator`` on the CPU, seeded, drawing in the fixed order
     XQ, XK, XV, eta-noise, W0 (TTT-MLP: W1 then W2), then optional extras;
   * XQ, XK, XV ~ N(0, 1) drawn in fp32 as [B, H, L, D] and rounded to bf16
-    (round to nearest even) when the workload is bf16;
-  * eta[h, t] = sigmoid(N(0, 1)) / 64, shared over the batch;
+    (round to nearest even) when the workload is bf16 (``scale`` multiplies
+    the draws before rounding: the large-magnitude range tests);
+  * eta[h, t] = sigmoid(N(0, 1)) / 64, shared over the batch (or, with
+    ``eta_per_batch=True``, eta[b, h, t] drawn the same way, after every other
+    draw, so the other values stay those of the shared case);
   * W0 ~ N(0, 0.02^2) per head, b0 = 0 (the TTTLinear init on the pages),
     LayerNorm gamma = 1, beta = 0 — unless ``rich=True``, which draws
     non-trivial b0, gamma, beta so that parity checks exercise every term.
@@ -58,15 +61,17 @@ def _dtype(name: str) -> torch.dtype:
 
 
 def make_inputs(B: int, H: int, L: int, *, D: int = D_HEAD, dtype: str = "f32", seed: int = 0,
-                mlp_hidden: int = 0, rich: bool = False, eta_scale: float = 1.0 / 64.0) -> dict:
+                mlp_hidden: int = 0, rich: bool = False, eta_scale: float = 1.0 / 64.0,
+                eta_per_batch: bool = False, scale: float = 1.0) -> dict:
     """Draw one problem.  Returns CPU tensors:
-    XQ, XK, XV [B, H, L, D] in ``dtype``; eta [H, L] fp32; ln_w, ln_b [H, D];
+    XQ, XK, XV [B, H, L, D] in ``dtype`` (N(0, scale^2)); eta [H, L] fp32
+    ([B, H, L] with ``eta_per_batch``); ln_w, ln_b [H, D];
     linear: W0 [H, D, D], b0 [H, D]; MLP: W1 [H, D, F], b1 [H, F], W2 [H, F, D], b2 [H, D]."""
     g = torch.Generator().manual_seed(seed)
     shape = (B, H, L, D)
-    XQ = torch.randn(shape, generator=g, dtype=torch.float32)
-    XK = torch.randn(shape, generator=g, dtype=torch.float32)
-    XV = torch.randn(shape, generator=g, dtype=torch.float32)
+    XQ = torch.randn(shape, generator=g, dtype=torch.float32) * scale
+    XK = torch.randn(shape, generator=g, dtype=torch.float32) * scale
+    XV = torch.randn(shape, generator=g, dtype=torch.float32) * scale
     eta = torch.sigmoid(torch.randn((H, L), generator=g, dtype=torch.float32)) * eta_scale
     out = {"XQ": XQ.to(_dtype(dtype)), "XK": XK.to(_dtype(dtype)), "XV": XV.to(_dtype(dtype)), "eta": eta}
     if mlp_hidden:
@@ -88,6 +93,8 @@ def make_inputs(B: int, H: int, L: int, *, D: int = D_HEAD, dtype: str = "f32", 
             out["b2"] = 0.05 * torch.randn((H, D), generator=g, dtype=torch.float32)
         else:
             out["b0"] = 0.05 * torch.randn((H, D), generator=g, dtype=torch.float32)
+    if eta_per_batch:
+        out["eta"] = torch.sigmoid(torch.randn((B, H, L), generator=g, dtype=torch.float32)) * eta_scale
     return out
 
 

@@ -58,7 +58,7 @@ class LinearGPU:
         sl = slice(t0, t1)
         fn = libttt.ttt_linear_decode if decode else libttt.ttt_linear_prefill
         fn(self.cfg, t1 - t0, self.x["XQ"][:, :, sl], self.x["XK"][:, :, sl], self.x["XV"][:, :, sl],
-           self.eta[:, sl], self.ln_w, self.ln_b, self.state, self.out[:, :, sl], token_eta=self.te)
+           self.eta[..., sl], self.ln_w, self.ln_b, self.state, self.out[:, :, sl], token_eta=self.te)
 
     def result(self):
         """out, W, b, and the dense W_grad (built from the open rows in the rows
@@ -85,7 +85,8 @@ def oracle_linear(inp: dict, *, K=16, rope=False, chains=None, L=None, token_eta
     for (b, h) in chains:
         q, k, v = (to_f64(inp[n][b, h, :L]) for n in ("XQ", "XK", "XV"))
         W, bb, G, gb = W0[h].copy(), b0[h].copy(), np.zeros((D, D)), np.zeros(D)
-        o = oracle.linear_chain(q, k, v, eta[h, :L], lw[h], lb[h], W, bb, G, gb, K=K, rope=rope, token_eta=token_eta)
+        e = eta[b, h, :L] if eta.ndim == 3 else eta[h, :L]
+        o = oracle.linear_chain(q, k, v, e, lw[h], lb[h], W, bb, G, gb, K=K, rope=rope, token_eta=token_eta)
         outs.append(o)
         Ws.append(W)
         bs.append(bb)
@@ -120,7 +121,7 @@ class MlpGPU:
         sl = slice(t0, t1)
         fn = libttt.ttt_mlp_decode if decode else libttt.ttt_mlp_prefill
         fn(self.cfg, t1 - t0, self.x["XQ"][:, :, sl], self.x["XK"][:, :, sl],
-                               self.x["XV"][:, :, sl], self.eta[:, sl], self.ln_w, self.ln_b, self.state,
+                               self.x["XV"][:, :, sl], self.eta[..., sl], self.ln_w, self.ln_b, self.state,
                                self.out[:, :, sl], token_eta=self.te)
 
     def result(self):
@@ -151,10 +152,51 @@ def oracle_mlp(inp: dict, *, K=16, rope=False, chains=None, L=None, token_eta=No
     for (b, h) in chains:
         q, k, v = (to_f64(inp[n][b, h, :L]) for n in ("XQ", "XK", "XV"))
         st = [a[h].copy() for a in init] + [np.zeros((D, F)), np.zeros(F), np.zeros((F, D)), np.zeros(D)]
-        o = oracle.mlp_chain(q, k, v, eta[h, :L], lw[h], lb[h], *st, K=K, rope=rope, token_eta=token_eta)
+        e = eta[b, h, :L] if eta.ndim == 3 else eta[h, :L]
+        o = oracle.mlp_chain(q, k, v, e, lw[h], lb[h], *st, K=K, rope=rope, token_eta=token_eta)
         for i, a in enumerate([o] + st):
             res[i].append(a)
     return tuple(np.stack(r) for r in res)
+
+
+def _eta_batch(inp, L):
+    """eta for the oracle's batch drivers: flat, head stride L, and its batch
+    stride (0 when shared over the batch)."""
+    eta = to_f64(inp["eta"])[..., :L]
+    if eta.ndim == 3:
+        return np.ascontiguousarray(eta), eta.shape[1] * L
+    return np.ascontiguousarray(eta), 0
+
+
+def oracle_linear_all(inp: dict, *, K=16, rope=False, L=None, token_eta=None):
+    """Every chain through the oracle's OpenMP batch driver (from W0, b0 tiled
+    over the batch).  Returns out [B, H, L, D], W, b, G, gb [B, H, ...]."""
+    B, H, Lf, D = inp["XQ"].shape
+    L = Lf if L is None else L
+    x = [np.ascontiguousarray(to_f64(inp[n][:, :, :L])) for n in ("XQ", "XK", "XV")]
+    eta, eta_sB = _eta_batch(inp, L)
+    W = np.ascontiguousarray(np.broadcast_to(to_f64(inp["W0"]), (B, H, D, D)))
+    b = np.ascontiguousarray(np.broadcast_to(to_f64(inp["b0"]), (B, H, D)))
+    G, gb = np.zeros_like(W), np.zeros_like(b)
+    out = oracle.linear_batch(*x, eta, eta_sB, to_f64(inp["ln_w"]), to_f64(inp["ln_b"]), W, b, G, gb, K=K,
+                              rope=rope, token_eta=token_eta)
+    return out, W, b, G, gb
+
+
+def oracle_mlp_all(inp: dict, *, K=16, rope=False, L=None, token_eta=None):
+    """Every chain of a TTT-MLP problem through the OpenMP batch driver.
+    Returns out [B, H, L, D] and the 8 state arrays [B, H, ...]."""
+    B, H, Lf, D = inp["XQ"].shape
+    F = inp["W1"].shape[-1]
+    L = Lf if L is None else L
+    x = [np.ascontiguousarray(to_f64(inp[n][:, :, :L])) for n in ("XQ", "XK", "XV")]
+    eta, eta_sB = _eta_batch(inp, L)
+    shapes = {"W1": (D, F), "b1": (F,), "W2": (F, D), "b2": (D,)}
+    st = [np.ascontiguousarray(np.broadcast_to(to_f64(inp[n]), (B, H) + shapes[n])) for n in ("W1", "b1", "W2", "b2")]
+    st += [np.zeros_like(a) for a in st]
+    out = oracle.mlp_batch(*x, eta, eta_sB, to_f64(inp["ln_w"]), to_f64(inp["ln_b"]), *st, K=K, rope=rope,
+                           token_eta=token_eta)
+    return (out,) + tuple(st)
 
 
 def max_abs(a, b) -> float:
@@ -167,5 +209,5 @@ def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
     return np.exp2(np.floor(np.log2(ax)) - 8)
 
 
-__all__ = ["LinearGPU", "oracle_linear", "MlpGPU", "oracle_mlp", "max_abs", "tol_for", "make_inputs", "to_f64", "bf16_half_ulp",
+__all__ = ["LinearGPU", "oracle_linear", "oracle_linear_all", "MlpGPU", "oracle_mlp", "oracle_mlp_all", "max_abs", "tol_for", "make_inputs", "to_f64", "bf16_half_ulp",
            "TOL_F32", "TOL_BF16"]

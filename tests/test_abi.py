@@ -105,6 +105,10 @@ CASES = [
     ("out overlaps XQ", dict(out=T.ttt_tensor(_addr(0) + 4096, H * L * D, L * D, D)), "TTT_ERR_ALIAS"),
     ("out overlaps state", dict(out=T.ttt_tensor(_addr(8), H * L * D, L * D, D)), "TTT_ERR_ALIAS"),
     ("out rows overlap", dict(out=T.ttt_tensor(_addr(10), H * L * D, L * D, 32)), "TTT_ERR_ALIAS"),
+    ("XQ overlaps W", dict(XQ=T.ttt_tensor(_addr(6) + 1024, H * L * D, L * D, D)), "TTT_ERR_ALIAS"),
+    ("eta overlaps b_grad", dict(eta=T.ttt_eta(_addr(9), 0, L)), "TTT_ERR_ALIAS"),
+    ("ln_b overlaps W_grad", dict(ln_b=_addr(8) + 512), "TTT_ERR_ALIAS"),
+    ("token_eta overlaps b", dict(eta=T.ttt_eta(_addr(3), 0, L, _addr(7))), "TTT_ERR_ALIAS"),
     ("state buffers overlap", dict(state=T.ttt_linear_state(_addr(6), _addr(6) + 64, _addr(8), _addr(9), 0)),
      "TTT_ERR_ALIAS"),
     ("negative offset", dict(state=T.ttt_linear_state(_addr(6), _addr(7), _addr(8), _addr(9), -3)),
@@ -182,6 +186,8 @@ MLP_CASES = [
     ("state buffers overlap", dict(state=_mlp_state(s3=_addr(20) + 1024)), "TTT_ERR_ALIAS"),
     ("out overlaps XK", dict(out=T.ttt_tensor(_addr(1), H * L * D, L * D, D)), "TTT_ERR_ALIAS"),
     ("out overlaps state", dict(out=T.ttt_tensor(_addr(24), H * L * D, L * D, D)), "TTT_ERR_ALIAS"),
+    ("XV overlaps W2", dict(XV=T.ttt_tensor(_addr(22), H * L * D, L * D, D)), "TTT_ERR_ALIAS"),
+    ("ln_w overlaps b1_grad", dict(ln_w=_addr(25)), "TTT_ERR_ALIAS"),
 ]
 
 

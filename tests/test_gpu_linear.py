@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 import torch
 
-from harness import (LinearGPU, bf16_half_ulp, make_inputs, max_abs, oracle_linear, tol_for)
+from harness import (LinearGPU, bf16_half_ulp, make_inputs, max_abs, oracle_linear_all, tol_for)
 from test_rnn_layers_amd.synth import WORKLOADS, workload_inputs
 
 pytestmark = pytest.mark.gpu
@@ -27,8 +27,7 @@ def _check_full(name, inp, *, dtype, rope=False, K=16, pieces=None, layout="bhld
     for i in range(len(cuts) - 1):
         g.run(cuts[i], cuts[i + 1], decode=cuts[i] in decode)
     out, W, b, G, gb = g.result()
-    ro, rW, rb, rG, rgb = oracle_linear(inp, K=K, rope=rope, token_eta=token_eta)
-    out = out.reshape(B * H, L, D)
+    ro, rW, rb, rG, rgb = oracle_linear_all(inp, K=K, rope=rope, token_eta=token_eta)
     err = max_abs(out, ro)
     tol = tol_for(dtype)
     if out_dtype == "bf16":
@@ -238,40 +237,40 @@ def test_minimum_inputs():
 
 
 # ---------------------------------------------------------------------------
-# full-size workloads: every output is produced, sampled chains are compared
-# with the oracle, all outputs checked finite
+# full-size workloads: every chain of the GPU run is compared with the oracle
+# (its OpenMP batch driver), every output and the final state
 # ---------------------------------------------------------------------------
-def _full_size(w, chains, *, rope):
+def _full_size(w, *, rope):
     inp = workload_inputs(w)
     B, H, L, D = inp["XQ"].shape
     g = LinearGPU(inp, rope=rope, in_dtype=w.dtype)
     g.run(0, L)
     out, W, b, _, _ = g.result()
     assert np.isfinite(out).all()
-    ro, rW, rb, _, _ = oracle_linear(inp, rope=rope, chains=chains)
-    errs = []
-    for i, (bb, h) in enumerate(chains):
-        errs.append(max_abs(out[bb, h], ro[i]))
-        assert max_abs(W[bb, h], rW[i]) <= tol_for(w.dtype) * max(1.0, np.abs(rW[i]).max())
-    # error per mini-batch index, to see drift along the chain
-    e_blocks = np.abs(out[chains[0][0], chains[0][1]] - ro[0]).reshape(-1, 16 * D).max(axis=1)
-    _report(w.name, err=max(errs), first_blocks=float(e_blocks[:8].max()), last_blocks=float(e_blocks[-8:].max()))
-    assert max(errs) <= tol_for(w.dtype)
+    ro, rW, rb, _, _ = oracle_linear_all(inp, rope=rope)
+    err = np.abs(out - ro).reshape(B * H, L // 16, 16 * D).max(axis=2)  # per chain and mini-batch
+    worst = int(err.max(axis=1).argmax())
+    tol = tol_for(w.dtype)
+    # error per mini-batch index of the worst chain, to see drift along the chain
+    _report(w.name, chains=B * H, err=float(err.max()), worst_chain=worst, first_blocks=float(err[worst, :8].max()),
+            last_blocks=float(err[worst, -8:].max()), W=max_abs(W, rW), b=max_abs(b, rb))
+    assert float(err.max()) <= tol
+    sc = max(1.0, float(np.abs(rW).max()))
+    assert max_abs(W, rW) <= tol * sc
+    assert max_abs(b, rb) <= tol * sc
 
 
 def test_full_125m_rope_workload():
-    w = WORKLOADS[1]
-    _full_size(w, [(0, 0), (3, 7), (7, 11)], rope=True)
+    _full_size(WORKLOADS[1], rope=True)
 
 
 def test_full_1b_workload():
-    w = WORKLOADS[2]
-    _full_size(w, [(0, 0), (2, 17), (3, 31)], rope=False)
+    _full_size(WORKLOADS[2], rope=False)
 
 
 def test_decode_workload():
-    """Prefill 512 tokens, then 256 single-token decode calls; compared with
-    the oracle on sampled chains and with one GPU prefill over all 768."""
+    """Prefill 512 tokens, then 256 single-token decode calls; every chain
+    compared with the oracle, and with one GPU prefill over all 768."""
     w = WORKLOADS[4]
     inp = workload_inputs(w)
     B, H, L, D = inp["XQ"].shape
@@ -284,18 +283,20 @@ def test_decode_workload():
     whole = LinearGPU(inp, in_dtype="bf16")
     whole.run(0, L)
     out2, W2, _, _, _ = whole.result()
-    chains = [(0, 0), (17, 5), (40, 31), (63, 12)]
-    ro, rW, _, rG, _ = oracle_linear(inp, chains=chains)
-    errs = [max_abs(out[bb, h], ro[i]) for i, (bb, h) in enumerate(chains)]
-    _report(w.name, err=max(errs), gpu_split_vs_whole=max_abs(out, out2))
-    assert max(errs) <= tol_for("bf16")
+    ro, rW, rb, _, _ = oracle_linear_all(inp)
+    err = max_abs(out, ro)
+    _report(w.name, chains=B * H, err=err, W=max_abs(W, rW), gpu_split_vs_whole=max_abs(out, out2))
+    assert err <= tol_for("bf16")
+    assert max_abs(W, rW) <= tol_for("bf16") * max(1.0, np.abs(rW).max())
+    assert max_abs(b, rb) <= tol_for("bf16") * max(1.0, np.abs(rW).max())
     assert max_abs(out, out2) <= tol_for("bf16")
     assert max_abs(W, W2) <= 1e-3 * max(1.0, np.abs(W2).max())
 
 
 def test_decode_workload_rows_layout():
-    """The decode workload with the rows layout: the same outputs and W, b as
-    the dense layout (to rounding), and the oracle on sampled chains."""
+    """The decode workload with the rows layout, stopped 5 tokens into a
+    mini-batch: every chain against the oracle (outputs, W, b and the open
+    gradients), and the same outputs and W as the dense layout (to rounding)."""
     w = WORKLOADS[4]
     inp = workload_inputs(w)
     B, H, L, D = inp["XQ"].shape
@@ -307,17 +308,57 @@ def test_decode_workload_rows_layout():
             g.run(t, t + 1, decode=True)
         res[layout] = g.result()
         assert g.state.offset == L - 5
-    chains = [(0, 0), (33, 9), (63, 31)]
-    ro, rW, rb, rG, rgb = oracle_linear(inp, chains=chains, L=L - 5)
+    ro, rW, rb, rG, rgb = oracle_linear_all(inp, L=L - 5)
     out, W, b, G, gb = res["rows"]
-    errs = [max_abs(out[bb, h, : L - 5], ro[i]) for i, (bb, h) in enumerate(chains)]
-    gerr = max(max_abs(G[bb, h], rG[i]) for i, (bb, h) in enumerate(chains))
-    _report(w.name + "_rows", err=max(errs), G=gerr, rows_vs_dense=max_abs(out[:, :, : L - 5], res["dense"][0][:, :, : L - 5]))
-    assert max(errs) <= tol_for("bf16")
-    assert gerr <= tol_for("bf16") * max(1.0, float(np.abs(rG).max()))
-    assert max_abs(out[:, :, : L - 5], res["dense"][0][:, :, : L - 5]) <= tol_for("bf16")
+    err = max_abs(out[:, :, : L - 5], ro)
+    gerr = max_abs(G, rG)
+    tol = tol_for("bf16")
+    _report(w.name + "_rows", chains=B * H, err=err, G=gerr, W=max_abs(W, rW),
+            rows_vs_dense=max_abs(out[:, :, : L - 5], res["dense"][0][:, :, : L - 5]))
+    assert err <= tol
+    assert gerr <= tol * max(1.0, float(np.abs(rG).max()))
+    assert max_abs(gb, rgb) <= tol * max(1.0, float(np.abs(rgb).max()))
+    assert max_abs(W, rW) <= tol * max(1.0, float(np.abs(rW).max()))
+    assert max_abs(out[:, :, : L - 5], res["dense"][0][:, :, : L - 5]) <= tol
     assert max_abs(W, res["dense"][1]) <= 1e-3 * max(1.0, np.abs(W).max())
     assert max_abs(G, res["dense"][3]) <= 1e-3 * max(1.0, np.abs(G).max())
+
+
+# per-batch learning rates, eta [B, H, L] ("代码连连看——TTT", compute_mini_batch
+# takes eta per batch and head): every kernel reads its chain's row
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_per_batch_eta_prefill(dtype):
+    """Open head, whole mini-batches (dual kernel) and a ragged tail, with a
+    learning rate that differs per batch row."""
+    inp = make_inputs(3, 2, 16 * 5 + 9, dtype=dtype, seed=401, rich=True, eta_per_batch=True)
+    assert inp["eta"].shape == (3, 2, 89)
+    _check_full(f"per_batch_eta_{dtype}", inp, dtype=dtype, rope=True, pieces=[5])
+
+
+@pytest.mark.parametrize("grad_layout", ["dense", "rows"])
+def test_per_batch_eta_decode(grad_layout):
+    """A prefill, then single-token decode calls across two commits, with a
+    per-batch learning rate."""
+    inp = make_inputs(3, 2, 56, dtype="bf16", seed=403, rich=True, eta_per_batch=True)
+    cuts = [21] + list(range(22, 56))
+    _check_full(f"per_batch_eta_decode_{grad_layout}", inp, dtype="bf16", pieces=cuts, decode=set(cuts),
+                grad_layout=grad_layout)
+
+
+def test_per_batch_eta_differs_from_shared():
+    """The per-batch rows are really used: the same problem with batch row 0's
+    rates shared over the batch gives the oracle's shared-rate result, not
+    the per-batch one (guards a kernel that reads row 0 for every chain)."""
+    inp = make_inputs(2, 2, 48, dtype="bf16", seed=405, rich=True, eta_per_batch=True)
+    g = LinearGPU(inp, in_dtype="bf16")
+    g.run(0, 48)
+    out = g.result()[0]
+    ro = oracle_linear_all(inp)[0]
+    shared = dict(inp)
+    shared["eta"] = inp["eta"][0]
+    rs = oracle_linear_all(shared)[0]
+    assert max_abs(out, ro) <= tol_for("bf16")
+    assert max_abs(out[1], rs[1]) > 10 * tol_for("bf16")
 
 
 def test_many_chains_bitwise_repeatable():

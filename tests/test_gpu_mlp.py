@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 import torch
 
-from harness import MlpGPU, TOL_BF16, bf16_half_ulp, make_inputs, max_abs, oracle_mlp
+from harness import MlpGPU, TOL_BF16, bf16_half_ulp, make_inputs, max_abs, oracle_mlp, oracle_mlp_all
 from test_rnn_layers_amd import libttt
 from test_rnn_layers_amd.synth import WORKLOADS, workload_inputs
 
@@ -46,8 +46,11 @@ def _run(name, inp, *, rope=False, pieces=(), out_dtype="f32", chains=None, toke
     for i in range(len(cuts) - 1):
         g.run(cuts[i], cuts[i + 1], decode=cuts[i] in decode)
     got = g.result()
-    chains = [(b, h) for b in range(B) for h in range(H)] if chains is None else chains
-    ref = oracle_mlp(inp, rope=rope, chains=chains, token_eta=token_eta, K=K)
+    if chains is None:  # every chain, through the oracle's OpenMP batch driver
+        chains = [(b, h) for b in range(B) for h in range(H)]
+        ref = [a.reshape((B * H,) + a.shape[2:]) for a in oracle_mlp_all(inp, rope=rope, token_eta=token_eta, K=K)]
+    else:
+        ref = oracle_mlp(inp, rope=rope, chains=chains, token_eta=token_eta, K=K)
     _compare(name, got, ref, chains, out_dtype=out_dtype, tol=tol)
     assert g.state.offset == L
     return got
@@ -196,24 +199,22 @@ def test_open_offset_continues():
     _run("mlp_open_continue", inp, pieces=(20,))
 
 
-def test_full_350m_workload_sampled():
-    """The 350M-shape TTT-MLP layer (B=4, H=16, L=4096) in one launch; the
-    oracle checks sampled chains, including the first and last."""
+def test_full_350m_workload():
+    """The 350M-shape TTT-MLP layer (B=4, H=16, L=4096) in one launch; every
+    chain's outputs and final state against the oracle."""
     w = next(x for x in WORKLOADS if x.kind == "mlp")
-    inp = workload_inputs(w)
-    B, H = w.B, w.H
-    _run(w.name, inp, chains=[(0, 0), (1, 7), (2, 11), (B - 1, H - 1)])
+    _run(w.name, workload_inputs(w))
 
 
-def test_decode_workload_sampled():
+def test_decode_workload():
     """The TTT-MLP decode workload (B16 H16: prefill 512 tokens in the dual
-    kernel, then 64 single-token decode calls in the token kernel); the oracle
-    checks sampled chains."""
+    kernel, then 64 single-token decode calls in the token kernel); every
+    chain against the oracle."""
     w = next(x for x in WORKLOADS if x.kind == "mlp_decode")
     inp = workload_inputs(w)
-    B, H, L = w.B, w.H, w.L
+    L = w.L
     cuts = [w.prefill] + list(range(w.prefill + 1, L))
-    _run(w.name, inp, pieces=cuts, decode=set(cuts), chains=[(0, 0), (7, 5), (B - 1, H - 1)])
+    _run(w.name, inp, pieces=cuts, decode=set(cuts))
 
 
 # --- the rows layout of the gradients (open rows [k | eta g1], [x2 | eta g2])
@@ -270,13 +271,35 @@ def test_rows_matches_dense():
         assert max_abs(x, y) <= TOL_BF16, max_abs(x, y)
 
 
-def test_rows_decode_workload_sampled():
+def test_rows_decode_workload():
     w = next(x for x in WORKLOADS if x.kind == "mlp_decode")
     inp = workload_inputs(w)
-    B, H, L = w.B, w.H, w.L
+    L = w.L
     cuts = [w.prefill] + list(range(w.prefill + 1, L))
-    _run(w.name + "_rows", inp, pieces=cuts, decode=set(cuts), chains=[(0, 0), (7, 5), (B - 1, H - 1)],
-         grad_layout="rows")
+    _run(w.name + "_rows", inp, pieces=cuts, decode=set(cuts), grad_layout="rows")
+
+
+# per-batch learning rates, eta [B, H, L] ("代码连连看——TTT", compute_mini_batch
+# takes eta per batch and head)
+def test_per_batch_eta_prefill():
+    """Open head (token kernel), whole mini-batches and an open tail (dual
+    kernel), with rates that differ per batch row."""
+    inp = make_inputs(3, 2, 16 * 4 + 7, dtype="bf16", seed=411, rich=True, mlp_hidden=256, eta_per_batch=True)
+    assert inp["eta"].shape == (3, 2, 71)
+    _run("mlp_per_batch_eta", inp, rope=True, pieces=(6,))
+
+
+@pytest.mark.parametrize("grad_layout", ["dense", "rows"])
+def test_per_batch_eta_decode(grad_layout):
+    inp = make_inputs(3, 2, 44, dtype="bf16", seed=413, rich=True, mlp_hidden=256, eta_per_batch=True)
+    cuts = [19] + list(range(20, 44))
+    _run(f"mlp_per_batch_eta_decode_{grad_layout}", inp, pieces=cuts, decode=set(cuts), grad_layout=grad_layout)
+
+
+def test_per_batch_eta_fp32_inputs():
+    """fp32 inputs (every token in the token kernel) with per-batch rates."""
+    inp = make_inputs(2, 2, 37, dtype="f32", seed=415, rich=True, mlp_hidden=256, eta_per_batch=True)
+    _run("mlp_per_batch_eta_f32", inp, in_dtype="f32", pieces=(11,), tol=1e-4)
 
 
 @pytest.mark.parametrize("grad_layout", ["dense", "rows"])

@@ -209,6 +209,42 @@ def _f64(t):
     return t.double().numpy()
 
 
+def host_cpu():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def with_thread_sweep(fn, budget, *a):
+    """fn(*a, budget) at the oracle's full thread count (the reported value),
+    then at 1, 2, 4, ... threads below it with a quarter of the budget each
+    (at least one unit of work per point)."""
+    import oracle
+
+    tmax = oracle.max_threads()
+    res = fn(*a, budget)
+    sweep = []
+    t = 1
+    try:
+        while t < tmax:
+            oracle.set_threads(t)
+            sweep.append({"threads": t, "value": fn(*a, budget / 4)["value"]})
+            t *= 2
+    finally:
+        oracle.set_threads(tmax)
+    sweep.append({"threads": tmax, "value": res["value"]})
+    model, nproc = host_cpu()
+    res.update({"cpu_model": model, "nproc": nproc, "thread_sweep": sweep})
+    return res
+
+
 def cpu_linear(inp, w, rope, budget):
     """The oracle over whole batch rows of the workload (all heads, full L,
     OpenMP over the chains), cycling through the rows until the time budget
@@ -293,6 +329,15 @@ def cpu_decode(inp, w, budget):
 # ---------------------------------------------------------------------------
 # workloads
 # ---------------------------------------------------------------------------
+def arithmetic(kind, in_dtype):
+    """The arithmetic the timed kernel computes in (not the input format)."""
+    if kind == "dual":
+        if in_dtype == "bf16":
+            return "bf16 in, fp16 MFMA operands (power-of-two range scaling), fp32 accumulate and state"
+        return "fp32 in, fp32 MFMA (16x16x4), fp32 state"
+    return f"{in_dtype} in, fp32 VALU arithmetic, fp32 state"
+
+
 def common(args, w, value, elapsed, dtype, extra_cfg):
     return {"metric": None, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / args.steps, "higher_is_better": True,
@@ -349,7 +394,8 @@ def bench_linear(args, w):
     elapsed = run_steps(args, step)
     per = linear_token_bytes(w.dtype, args.out_dtype)
     amount = per * B * H * L + LINEAR_STATE_BYTES * B * H
-    res = common(args, w, B * L * args.steps / elapsed, elapsed, w.dtype, {"L": L, "rope": rope})
+    res = common(args, w, B * L * args.steps / elapsed, elapsed, arithmetic("dual", w.dtype),
+                 {"L": L, "rope": rope})
     res["metric"] = ("TTT-Linear prefill tokens/sec (1B shape, L=8192) + % of HBM/MFMA roofline"
                      if w.name.startswith("linear_1b") else f"TTT-Linear prefill tokens/sec ({w.name})")
     res["roofline"] = roofline("linear_dual_kernel", w.name + ("_rope" if rope and not w.rope else ""),
@@ -357,7 +403,7 @@ def bench_linear(args, w):
                                per_unit=f"{per} B per token-head + {LINEAR_STATE_BYTES} B state per chain",
                                units=f"{B * H * L} token-heads, {B * H} chains")
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_linear(inp, w, rope, args.cpu_seconds)
+        res["cpu_baseline"] = with_thread_sweep(cpu_linear, args.cpu_seconds, inp, w, rope)
     return res
 
 
@@ -393,9 +439,8 @@ def bench_mlp(args, w):
     elapsed = run_steps(args, step)
     nblk = (L + K - 1) // K
     amount = MLP_FLOPS_PER_BLOCK * B * H * nblk
-    res = common(args, w, B * L * args.steps / elapsed, elapsed, "bf16 in, fp16 MFMA operands, fp32 state",
+    res = common(args, w, B * L * args.steps / elapsed, elapsed, arithmetic("dual", w.dtype),
                  {"L": L, "mlp_hidden": F, "rope": False})
-    res["dtype"] = w.dtype
     res["metric"] = f"TTT-MLP prefill tokens/sec ({w.name})"
     res["roofline"] = roofline("mlp_dual_kernel", w.name, bound="mfma", amount=amount,
                                kernel_ms=stats(tm.ms("prefill")),
@@ -406,7 +451,7 @@ def bench_mlp(args, w):
     res["roofline"]["note"] = ("64 chains on 256 CUs: one workgroup per chain, so at most a quarter of the "
                                "chip's matrix cores can be busy")
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_mlp(inp, w, args.cpu_seconds)
+        res["cpu_baseline"] = with_thread_sweep(cpu_mlp, args.cpu_seconds, inp, w)
     return res
 
 
@@ -493,7 +538,7 @@ def bench_decode(args, w):
     else:
         kms = stats(tm.ms("token"))
         how = "256 decode calls launched one by one from Python; per-call HIP events"
-    res = common(args, w, B * T / (dec["mean"] * 1e-3), elapsed, w.dtype,
+    res = common(args, w, B * T / (dec["mean"] * 1e-3), elapsed, arithmetic("token", w.dtype),
                  {"prefill": P, "decode_steps": T, "rope": w.rope, "decode_launch": how,
                   "grad_layout": args.grad_layout,
                   "decode_phase_ms": dec, "prefill_ms": stats(tm.ms("prefill")),
@@ -505,7 +550,7 @@ def bench_decode(args, w):
                                         f"({args.grad_layout} W_grad, mean over the decode positions)",
                                units=f"{B * H} chains, one token each")
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_decode(inp, w, args.cpu_seconds)
+        res["cpu_baseline"] = with_thread_sweep(cpu_decode, args.cpu_seconds, inp, w)
     return res
 
 
@@ -596,7 +641,7 @@ def bench_mlp_decode(args, w):
     state_rw = mlp_decode_state_bytes(args.grad_layout, range(P, P + T))
     amount = (per_tok + state_rw) * B * H
     kms = {k: (v / T if k != "n" else v * T) for k, v in dec.items()}
-    res = common(args, w, B * T / (dec["mean"] * 1e-3), elapsed, w.dtype,
+    res = common(args, w, B * T / (dec["mean"] * 1e-3), elapsed, arithmetic("token", w.dtype),
                  {"prefill": P, "decode_steps": T, "mlp_hidden": F, "grad_layout": args.grad_layout,
                   "decode_launch": f"HIP graph of the {T} decode calls, replayed; per-call time = replay time / {T}",
                   "decode_phase_ms": dec,
@@ -607,7 +652,7 @@ def bench_mlp_decode(args, w):
                                         f"({args.grad_layout} gradients, mean over the decode positions)",
                                units=f"{B * H} chains, one token each")
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_mlp_decode(inp, w, args.cpu_seconds)
+        res["cpu_baseline"] = with_thread_sweep(cpu_mlp_decode, args.cpu_seconds, inp, w)
     return res
 
 

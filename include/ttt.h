@@ -237,8 +237,13 @@ typedef struct ttt_mlp_state {
     int64_t offset;
 } ttt_mlp_state;
 
-/* W1 [H, D, F], b1 [H, F], W2 [H, F, D], b2 [H, D] fp32 device, contiguous.
- * Tiles them over the batch, zeroes the gradients, sets offset = 0. */
+/* Initial state from the layer parameters.  The pages give only the linear
+ * layer's initial state ("TTTLinear.ttt": W1, b1 tiled over the batch) and
+ * describe TTT-MLP as two such layers stacked ("代码连连看——TTT", the remark
+ * after compute_mini_batch); this call applies the same tiling to all four
+ * parameters.  W1 [H, D, F], b1 [H, F], W2 [H, F, D], b2 [H, D] fp32 device,
+ * contiguous.  Tiles them over the batch, zeroes the gradients, sets
+ * offset = 0. */
 ttt_status ttt_mlp_state_init(const ttt_mlp_cfg *cfg, const float *W1, const float *b1, const float *W2,
                               const float *b2, ttt_mlp_state *state, void *stream);
 

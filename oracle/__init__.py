@@ -18,4 +18,5 @@ from .oracle import (  # noqa: F401
     linear_batch,
     mlp_batch,
     max_threads,
+    set_threads,
 )

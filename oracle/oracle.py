@@ -64,6 +64,7 @@ def load():
     lib.oracle_mlp_batch.argtypes = ([_i32] * 6 + [_i64, _dp, _dp, _dp, _dp, _i64, _dp, _dp, _dp, _i32, _f64, _f64]
                                      + [_dp] * 9)
     lib.oracle_max_threads.restype = _i32
+    lib.oracle_set_threads.argtypes = [_i32]
     _lib = lib
     return lib
 
@@ -198,3 +199,8 @@ def mlp_batch(XQ, XK, XV, eta, eta_sB, ln_w, ln_b, W1, b1, W2, b2, G1, gb1, G2, 
 
 def max_threads() -> int:
     return int(load().oracle_max_threads())
+
+
+def set_threads(n: int) -> None:
+    """Thread count of the batch drivers from now on."""
+    load().oracle_set_threads(int(n))

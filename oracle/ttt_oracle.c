@@ -555,3 +555,13 @@ int oracle_max_threads(void)
     return 1;
 #endif
 }
+
+/* Thread count of the batch drivers' parallel loops from now on (n >= 1). */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

@@ -6,9 +6,6 @@
 
 namespace ttt {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 64;      // head_dim handled by every kernel
@@ -83,25 +80,6 @@ __device__ __forceinline__ void wave_sum2(float &x, float &y) {
     y += dpp_mov<0x140>(y);
     x = rows_total(x);
     y = rows_total(y);
-}
-
-// 16x16x32 bf16 MFMA, fp32 accumulate.
-// Lane l (g = l/16, n = l%16): A holds A[n][8g .. 8g+7], B holds B[8g .. 8g+7][n],
-// C/D holds C[4g .. 4g+3][n].
-__device__ __forceinline__ f32x4 mfma_k32(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-// 16x16x16 bf16 MFMA, fp32 accumulate.  A holds A[n][4g .. 4g+3],
-// B holds B[4g .. 4g+3][n], C/D as above.
-__device__ __forceinline__ f32x4 mfma_k16(bf16x4 a, bf16x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
-                                                      __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
-}
-
-// Split x into a bf16 pair with x ~= hi + lo (error ~2^-17 |x|).
-__device__ __forceinline__ void split_bf16(float x, __bf16 &hi, __bf16 &lo) {
-    hi = (__bf16)x;
-    lo = (__bf16)(x - (float)hi);
 }
 
 }  // namespace ttt

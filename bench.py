@@ -165,10 +165,10 @@ def run_steps(args, step):
     return time.perf_counter() - t0
 
 
-def measured_traffic(kernel, workload):
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    runs, if they were taken on the kernel source as it is now."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def _profile_record(name, kernel, workload):
+    """A committed rocprofv3 record of this kernel and workload, if it was
+    taken on the kernel source as it is now."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -177,7 +177,24 @@ def measured_traffic(kernel, workload):
 
     if not rec or rec.get("source_sha256") != source_digest(kernel):
         return None
-    return rec["hbm_bytes_per_launch"]
+    return rec
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the FETCH_SIZE / WRITE_SIZE runs."""
+    rec = _profile_record("traffic.json", kernel, workload)
+    return None if rec is None else rec["hbm_bytes_per_launch"]
+
+
+def measured_mfma(kernel, workload):
+    """Matrix-core busy fraction from SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE."""
+    rec = _profile_record("mfma.json", kernel, workload)
+    if rec is None:
+        return None
+    return {"busy_frac_chip": rec["mfma_busy_frac_chip"],
+            "busy_frac_occupied_cus": rec["mfma_busy_frac_occupied_cus"],
+            "occupied_cus": rec["occupied_cus"], "counter_flops": rec["counter_flops"],
+            "source": "rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs"}
 
 
 def roofline(kernel, workload, *, bound, amount, kernel_ms, per_unit, units):
@@ -185,7 +202,8 @@ def roofline(kernel, workload, *, bound, amount, kernel_ms, per_unit, units):
     scale = 1e9 if bound == "hbm" else 1e12
     achieved = amount / (kernel_ms["mean"] * 1e-3) / scale
     return {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
-            "traffic": measured_traffic(kernel, workload), "kernel": kernel, "kernel_ms": kernel_ms,
+            "traffic": measured_traffic(kernel, workload), "mfma_util_counter": measured_mfma(kernel, workload),
+            "kernel": kernel, "kernel_ms": kernel_ms,
             "algorithmic_per_launch": amount, "algorithmic_per_unit": per_unit, "units_per_launch": units}
 
 

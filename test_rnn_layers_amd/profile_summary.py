@@ -11,8 +11,14 @@ sources, and the per-launch HBM traffic record that bench.py reports.
         --kernel linear_dual_kernel --workload linear_1b_B4_H32_L8192_bf16 --copy-mb 1024 \
         --cmd "<the two rocprofv3 commands>" --out profiles/linear_dual_kernel_linear_1b_traffic.md
 
-The counters read KiB per dispatch; each is scaled by the ratio of the copy's
-known byte count to what the same counter read for the copy.
+    # matrix-core use: one --pmc run with SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE
+    # and the SQ_INSTS_VALU_MFMA_MOPS_* counters
+    python -m test_rnn_layers_amd.profile_summary mfma DIR --kernel linear_dual_kernel \
+        --workload linear_1b_B4_H32_L8192_bf16 --workgroups 128 --flops 30064771072 \
+        --cmd "<the rocprofv3 command>" --out profiles/linear_dual_kernel_linear_1b_mfma.md
+
+The byte counters read KiB per dispatch; each is scaled by the ratio of the
+copy's known byte count to what the same counter read for the copy.
 """
 from __future__ import annotations
 
@@ -30,6 +36,10 @@ ROOT = os.path.dirname(PKG)
 KERNEL_SOURCES = {"linear_dual_kernel": "linear_dual.hip", "mlp_dual_kernel": "mlp_dual.hip",
                   "linear_token_kernel": "linear_token.hip", "mlp_token_kernel": "mlp_token.hip"}
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+MFMA_JSON = os.path.join(ROOT, "profiles", "mfma.json")
+SIMDS_PER_CU = 4
+CUS = 256
+XCCS = 8  # GRBM_GUI_ACTIVE is reported once per XCC; the dispatch's cycles are their maximum
 
 
 def source_digest(kernel: str) -> str:
@@ -104,11 +114,7 @@ def traffic_summary(fetch_dir, write_dir, kernel, workload, copy_mb, cmd):
            "hbm_bytes_per_launch": fb + wb, "fetch_kib_raw": statistics.median(kf),
            "write_kib_raw": statistics.median(kw), "copy_fetch_kib": cf, "copy_write_kib": cw,
            "fetch_scale": sf, "write_scale": sw, "dispatches": [len(kf), len(kw)]}
-    db = json.load(open(TRAFFIC_JSON)) if os.path.exists(TRAFFIC_JSON) else {}
-    db[f"{kernel}@{workload}"] = rec
-    with open(TRAFFIC_JSON, "w") as fh:
-        json.dump(db, fh, indent=1, sort_keys=True)
-        fh.write("\n")
+    _record(TRAFFIC_JSON, f"{kernel}@{workload}", rec)
     lines = [f"# HBM traffic of {kernel} ({workload})", "", "Commands:", "", "```", cmd, "```", "",
              f"- copy probe: {copy_bytes} bytes read and written; FETCH_SIZE read {cf:.0f} KiB, WRITE_SIZE "
              f"{cw:.0f} KiB -> scale {sf:.4f} (fetch), {sw:.4f} (write)",
@@ -116,6 +122,54 @@ def traffic_summary(fetch_dir, write_dir, kernel, workload, copy_mb, cmd):
              f"per dispatch (median of {len(kf)} / {len(kw)})",
              f"- scaled: {fb / 1e6:.1f} MB read + {wb / 1e6:.1f} MB written = {(fb + wb) / 1e6:.1f} MB per launch",
              f"- kernel source sha256 {rec['source_sha256'][:16]}..."]
+    return "\n".join(lines) + "\n"
+
+
+def _record(path, key, rec):
+    db = json.load(open(path)) if os.path.exists(path) else {}
+    db[key] = rec
+    with open(path, "w") as fh:
+        json.dump(db, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+
+
+def mfma_summary(d, kernel, workload, workgroups, flops, cmd):
+    """Matrix-core use of one kernel from SQ_VALU_MFMA_BUSY_CYCLES (cycles a
+    SIMD's matrix core is busy, summed over SIMDs) against GRBM_GUI_ACTIVE
+    (the dispatch's GPU cycles, summed over the XCCs), and the flops the MFMA
+    op counters report (SQ_INSTS_VALU_MFMA_MOPS_*: units of 512 flops)."""
+    names = ["SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_F16",
+             "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_INSTS_MFMA"]
+    per = {}
+    for nm in names:
+        v = [x for (k, g, x) in _counter(d, nm) if kernel in k]
+        if v:
+            per[nm] = statistics.median(v)
+    if "SQ_VALU_MFMA_BUSY_CYCLES" not in per or "GRBM_GUI_ACTIVE" not in per:
+        raise SystemExit(f"no {kernel} dispatches with SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE")
+    cycles = per["GRBM_GUI_ACTIVE"] / XCCS
+    busy = per["SQ_VALU_MFMA_BUSY_CYCLES"]
+    chip = busy / (cycles * CUS * SIMDS_PER_CU)
+    held = busy / (cycles * min(workgroups, CUS) * SIMDS_PER_CU)
+    mops = sum(per.get(n, 0.0) for n in names[2:5])
+    rec = {"source_sha256": source_digest(kernel), "mfma_busy_frac_chip": chip,
+           "mfma_busy_frac_occupied_cus": held, "occupied_cus": min(workgroups, CUS), "dispatch_cycles": cycles,
+           "mfma_busy_simd_cycles": busy, "counter_flops": mops * 512, "algorithmic_flops": flops,
+           "counters": per}
+    _record(MFMA_JSON, f"{kernel}@{workload}", rec)
+    lines = [f"# Matrix-core use of {kernel} ({workload})", "", "Command:", "", "```", cmd, "```", "",
+             "| counter | median per dispatch |", "|---|---|"]
+    for k in names:
+        if k in per:
+            lines.append(f"| {k} | {per[k]:.6g} |")
+    lines += ["",
+              f"- dispatch: {cycles:.0f} GPU cycles (GRBM_GUI_ACTIVE / {XCCS} XCCs)",
+              f"- MFMA busy: {busy:.4g} SIMD-cycles = **{chip:.2%} of the chip's {CUS * SIMDS_PER_CU} SIMDs** "
+              f"over the dispatch; {held:.2%} of the {min(workgroups, CUS) * SIMDS_PER_CU} SIMDs of the "
+              f"{min(workgroups, CUS)} CUs that hold a workgroup",
+              f"- MFMA flops by op counters: {mops * 512:.4g}" + (
+                  f" (algorithmic {flops:.4g}: ratio {mops * 512 / flops:.3f})" if flops else ""),
+              f"- kernel source sha256 {rec['source_sha256'][:16]}..."]
     return "\n".join(lines) + "\n"
 
 
@@ -179,11 +233,21 @@ def main():
     q.add_argument("--blocks-per-chain", type=int, default=0, help="mini-batches per chain (per-mini-batch figures)")
     q.add_argument("--cmd", required=True)
     q.add_argument("--out", required=True)
+    f = sub.add_parser("mfma")
+    f.add_argument("dir")
+    f.add_argument("--kernel", required=True)
+    f.add_argument("--workload", required=True)
+    f.add_argument("--workgroups", type=int, required=True, help="workgroups per dispatch (one per CU)")
+    f.add_argument("--flops", type=float, default=0.0, help="algorithmic MFMA flops per dispatch")
+    f.add_argument("--cmd", required=True)
+    f.add_argument("--out", required=True)
     a = ap.parse_args()
     if a.cmd_name == "stats":
         text = stats_summary(a.dir, a.kernel, a.cmd)
     elif a.cmd_name == "sq":
         text = sq_summary(a.dirs, a.kernel, a.cmd, a.blocks_per_chain)
+    elif a.cmd_name == "mfma":
+        text = mfma_summary(a.dir, a.kernel, a.workload, a.workgroups, a.flops, a.cmd)
     else:
         text = traffic_summary(a.fetch, a.write, a.kernel, a.workload, a.copy_mb, a.cmd)
     os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)

@@ -202,6 +202,39 @@ struct Op<float> {
     __device__ static void put(float *p, float x) { *p = x; }
 };
 
+// Phase stamps: in a build with TTT_PHASE_STAMPS defined (an instrumentation
+// build; the library is built without it), lane 0 of each wave records the
+// low 32 bits of the shader clock at the phase boundaries of mini-batches
+// kStampFirst .. kStampFirst + kStampSteps - 1 in LDS; at the end, workgroup 0
+// copies them to stamps[(j * 8 + wave) * 8 + k] (j = m - kStampFirst), a
+// device buffer given by ttt_phase_stamps_set.  Otherwise the stamps compile
+// to nothing.
+#ifdef TTT_PHASE_STAMPS
+constexpr int kStampFirst = 256, kStampSteps = 64;
+__device__ unsigned int *g_phase_stamps;
+struct Stamps {
+    unsigned int t[kStampSteps][8][8];
+};
+__device__ __forceinline__ void phase_stamp(Stamps &st, int m, int k) {
+    __builtin_amdgcn_sched_barrier(0);
+    const unsigned int t = (unsigned int)__builtin_amdgcn_s_memtime();
+    const int j = m - kStampFirst;
+    if (j >= 0 && j < kStampSteps && (threadIdx.x & 63) == 0) st.t[j][threadIdx.x >> 6][k] = t;
+    __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void stamps_out(const Stamps &st) {
+    if (blockIdx.x != 0) return;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    for (int i = l; i < kStampSteps * 8; i += 64) {
+        const int j = i >> 3, k = i & 7;
+        g_phase_stamps[(j * 8 + w) * 8 + k] = st.t[j][w][k];
+    }
+}
+#define PHASE_STAMP(m, k) phase_stamp(sm.stamps, m, k)
+#else
+#define PHASE_STAMP(m, k) ((void)0)
+#endif
+
 // ---------------------------------------------------------------------------
 // LDS
 // ---------------------------------------------------------------------------
@@ -217,6 +250,9 @@ struct Smem {
     float zbuf[kM][kFP];            // Z_n: written by column waves, read by row waves
     float zbbuf[2][kM][kFP];        // Zbar_n, double-buffered (read two steps later)
     T gm[kM][Op<T>::GP];            // ng, row-major [token][column]
+#ifdef TTT_PHASE_STAMPS
+    Stamps stamps;
+#endif
 };
 
 // ---------------------------------------------------------------------------
@@ -236,6 +272,7 @@ __device__ __forceinline__ float row_sum16(float x) {
 }
 // value of lane (n + 8) mod 16 of the row (the lane holding columns +-32)
 __device__ __forceinline__ float row_swap8(float x) { return dpp<0x128>(x); }  // row_ror:8
+
 
 // workgroup barrier that the instruction scheduler cannot move work across
 // (s_barrier alone only orders memory operations): work placed between two
@@ -486,16 +523,22 @@ __device__ void row_main(const LinearArgs &a, Smem<T> &sm, int bi, int hi, int r
     // slot (m+2) % 4 = (m-2) % 4 = i, slot m % 4 = (2+i) % 4.
     auto step = [&](int m, auto I) {
         constexpr int i = decltype(I)::value;
+        PHASE_STAMP(m, 0);
         R.ln_forward(sm, rr[i], m - 2);
+        PHASE_STAMP(m, 1);
         // slot i is reused by the staging below: finish reading it first
         __builtin_amdgcn_sched_barrier(0);
         R.stage(sm.st[i], pf[i], rr[i]);
+        PHASE_STAMP(m, 2);
         // consume the register set before refilling it, so the refill lands in
         // the same registers (no copies that would wait on the new loads)
         __builtin_amdgcn_sched_barrier(0);
         R.fetch(pf[i]);  // m + 6
+        PHASE_STAMP(m, 3);
         phase_barrier();  // Z_m written
+        PHASE_STAMP(m, 4);
         R.ln_backward(sm, rr[(2 + i) % kRing]);
+        PHASE_STAMP(m, 5);
         phase_barrier();  // ng_m ready, Zbar_m-1 written
     };
     // after the last step, with N = m + r (m = 2 mod 4): Zbar_N-2, Zbar_N-1
@@ -617,11 +660,14 @@ __device__ void col_main(const LinearArgs &a, Smem<T> &sm, int ch, int c, int g,
 
     for (int m = 1; m < N; ++m) {
         // phase 1, the sequential chain: Z_m = Y_m + C_m-1 ng_m-1
+        PHASE_STAMP(m, 0);
         const F4 gf = O::load_b(&sm.gm[0][0], 16 * c + n, g);
         const f32x4 Z = O::mma16(Cf, gf, Y);
 #pragma unroll
         for (int j = 0; j < 4; ++j) sm.zbuf[4 * g + j][16 * c + n] = Z[j];
+        PHASE_STAMP(m, 1);
         phase_barrier();  // Z_m written
+        PHASE_STAMP(m, 2);
 
         // phase 2 (row waves run the LayerNorm of Z_m): Zbar_m-1, W_m, b_m,
         // then the products of mini-batch m with W_m
@@ -642,6 +688,7 @@ __device__ void col_main(const LinearArgs &a, Smem<T> &sm, int ch, int c, int g,
         Cf = O::make(scaled(O::xx(kxn, kx1, one), tl));
         O::kt_frags(kxn, sel, kt);
         kxn = kx1;
+        PHASE_STAMP(m, 3);
         phase_barrier();  // ng_m ready, Zbar_m-1 written
     }
     {
@@ -680,6 +727,9 @@ __global__ __launch_bounds__(512, kWavesPerSimd<T>) void linear_dual_kernel(Line
         col_main<T, TE>(a, sm, ch, w, g, n);
     else
         row_main<Tin, Tout, T, ROPE>(a, sm, bi, hi, w - 4, g, n);
+#ifdef TTT_PHASE_STAMPS
+    stamps_out(sm.stamps);
+#endif
 }
 
 template <typename Tin, typename Tout, typename T, bool ROPE, bool TE>
@@ -700,6 +750,12 @@ hipError_t launch_rope(const LinearArgs &a, hipStream_t s) {
 }
 
 }  // namespace
+
+#ifdef TTT_PHASE_STAMPS
+extern "C" int ttt_phase_stamps_set(unsigned int *buf) {
+    return (int)hipMemcpyToSymbol(HIP_SYMBOL(g_phase_stamps), &buf, sizeof(buf));
+}
+#endif
 
 hipError_t launch_linear_dual(const LinearArgs &a, int in_bf16, int out_bf16, hipStream_t s) {
     if (in_bf16 && out_bf16) return launch_rope<__bf16, __bf16, _Float16>(a, s);

@@ -18,5 +18,6 @@ from .oracle import (  # noqa: F401
     linear_batch,
     mlp_batch,
     max_threads,
+    post_proj,
     set_threads,
 )

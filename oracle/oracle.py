@@ -63,6 +63,7 @@ def load():
                                                        _f64] + [_dp] * 5)
     lib.oracle_mlp_batch.argtypes = ([_i32] * 6 + [_i64, _dp, _dp, _dp, _dp, _i64, _dp, _dp, _dp, _i32, _f64, _f64]
                                      + [_dp] * 9)
+    lib.oracle_post_proj.argtypes = [_i64, _i32, _i32, _dp, _dp, _dp, _f64, _dp, _dp, _dp]
     lib.oracle_max_threads.restype = _i32
     lib.oracle_set_threads.argtypes = [_i32]
     _lib = lib
@@ -194,6 +195,19 @@ def mlp_batch(XQ, XK, XV, eta, eta_sB, ln_w, ln_b, W1, b1, W2, b2, G1, gb1, G2, 
     load().oracle_mlp_batch(B, H, D, F, K, L, offset, _p(XQ), _p(XK), _p(XV), _p(eta), eta_sB, tp, _p(ln_w),
                             _p(ln_b), int(rope), rope_base, eps, _p(W1), _p(b1), _p(W2), _p(b2), _p(G1),
                             _p(gb1), _p(G2), _p(gb2), _p(out))
+    return out
+
+
+def post_proj(y, gamma, beta, Wo, bias=None, eps=1e-6):
+    """out = LayerNorm(y) Wo (+ bias) row by row: y [M, K], gamma/beta [K],
+    Wo [K, N], bias [N] or None.  Returns [M, N] float64."""
+    y, gamma, beta, Wo = map(_f, (y, gamma, beta, Wo))
+    M, K = y.shape
+    N = Wo.shape[1]
+    assert Wo.shape[0] == K and gamma.shape == (K,) and beta.shape == (K,)
+    out = np.empty((M, N))
+    bp = _p(_f(bias)) if bias is not None else None
+    load().oracle_post_proj(M, K, N, _p(y), _p(gamma), _p(beta), eps, _p(Wo), bp, _p(out))
     return out
 
 

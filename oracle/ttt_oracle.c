@@ -547,6 +547,34 @@ void oracle_mlp_batch(int B, int H, int D, int F, int K, int L, int64_t offset,
     }
 }
 
+/* ---------------------------------------------------------------------- */
+/* Post-norm and output projection of the layer output.  [P3 TTTBase.forward:
+ * after the scan the heads' outputs are concatenated to [B, L, width]
+ * (width = heads x head_dim), then post_norm, a LayerNorm over the width,
+ * then o_proj, a linear map.]  The LayerNorm is the one of ln_fwd above
+ * (population variance, eps inside the square root).  The pages show
+ * neither module's constructor: o_proj is read as a plain matrix Wo
+ * [K, N] with an optional bias (NULL for none).
+ * y [M, K] (rows = tokens), gamma, beta [K], Wo [K, N], out [M, N].
+ * Rows are independent: a caller may pass any subset of rows.           */
+/* ---------------------------------------------------------------------- */
+void oracle_post_proj(int64_t M, int K, int N, const double *y,
+                      const double *gamma, const double *beta, double eps,
+                      const double *Wo, const double *bias, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        double *x = (double *)malloc((size_t)K * sizeof(double));
+        oracle_ln_fwd(y + m * K, gamma, beta, K, eps, x);
+        for (int n = 0; n < N; ++n) {
+            double acc = bias ? bias[n] : 0.0;
+            for (int k = 0; k < K; ++k) acc += x[k] * Wo[(int64_t)k * N + n];
+            out[m * N + n] = acc;
+        }
+        free(x);
+    }
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP

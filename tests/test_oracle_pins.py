@@ -605,3 +605,68 @@ def test_batch_drivers_open_state_and_offset(orc):
     np.testing.assert_array_equal(out, ref_out)
     for a, x in zip(st, ref_state):
         np.testing.assert_array_equal(a, x)
+
+
+# ----------------------------------------------------------------------------
+# Post-norm and output projection ("代码连连看——TTT", TTTBase.forward: the
+# concatenated output goes through post_norm, a LayerNorm, then o_proj)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("K,N,bias", [(8, 3, False), (64, 48, True), (192, 64, False)])
+def test_post_proj_matches_library(orc, K, N, bias):
+    """Against torch: layer_norm over the width, then a matrix product."""
+    r = _rng(K + N)
+    y = r.normal(size=(7, K)) * r.uniform(0.1, 4, size=(7, 1)) + r.normal(size=(7, 1)) * 3
+    gam, bet = r.normal(size=K), r.normal(size=K)
+    Wo = r.normal(size=(K, N)) * 0.05
+    bv = r.normal(size=N) if bias else None
+    ref = Fn.layer_norm(torch.tensor(y), (K,), torch.tensor(gam), torch.tensor(bet), EPS) @ torch.tensor(Wo)
+    if bias:
+        ref = ref + torch.tensor(bv)
+    np.testing.assert_allclose(orc.post_proj(y, gam, bet, Wo, bv, EPS), ref.numpy(), rtol=1e-11, atol=1e-11)
+
+
+def test_post_proj_hand_example(orc):
+    """A 2 x 4 case worked by hand (eps = 0): the row (1, 3, 5, 7) has mean 4
+    and population variance 5, so LN gives (-3, -1, 1, 3) / sqrt(5); with
+    gamma = 1, beta = (1, 0, 0, 0) and Wo = e_1 + e_4 (column 0) and all ones
+    (column 1), the outputs are 1 + 0 and 1.  A constant row has variance 0:
+    not allowed with eps = 0, so eps = 1 there: LN = 0, outputs beta Wo = (1, 1)."""
+    y = np.array([[1.0, 3.0, 5.0, 7.0]])
+    Wo = np.array([[1.0, 1.0], [0.0, 1.0], [0.0, 1.0], [1.0, 1.0]])
+    gam, bet = np.ones(4), np.array([1.0, 0.0, 0.0, 0.0])
+    out = orc.post_proj(y, gam, bet, Wo, None, 0.0)
+    np.testing.assert_allclose(out, [[1.0 + 0.0, 1.0]], rtol=0, atol=1e-15)
+    out = orc.post_proj(np.full((1, 4), 2.5), gam, bet, Wo, None, 1.0)
+    np.testing.assert_allclose(out, [[1.0, 1.0]], rtol=0, atol=1e-15)
+
+
+def test_post_proj_invariances(orc):
+    """LayerNorm removes a per-row offset, and with eps = 0 a per-row positive
+    scale; gamma = 0 leaves beta Wo (+ bias) on every row; the map is linear
+    in (Wo, bias)."""
+    r = _rng(5)
+    K, N = 32, 24
+    y = r.normal(size=(6, K))
+    gam, bet = r.normal(size=K), r.normal(size=K)
+    Wo, bv = r.normal(size=(K, N)), r.normal(size=N)
+    base = orc.post_proj(y, gam, bet, Wo, bv, 0.0)
+    shifted = orc.post_proj(y + r.normal(size=(6, 1)) * 10, gam, bet, Wo, bv, 0.0)
+    scaled = orc.post_proj(y * r.uniform(0.1, 10, size=(6, 1)), gam, bet, Wo, bv, 0.0)
+    np.testing.assert_allclose(shifted, base, rtol=1e-9, atol=1e-9)
+    np.testing.assert_allclose(scaled, base, rtol=1e-9, atol=1e-9)
+    flat = orc.post_proj(y, np.zeros(K), bet, Wo, bv, EPS)
+    np.testing.assert_allclose(flat, np.broadcast_to(bet @ Wo + bv, (6, N)), rtol=1e-12, atol=1e-12)
+    W2, b2 = r.normal(size=(K, N)), r.normal(size=N)
+    lin = orc.post_proj(y, gam, bet, Wo + 2 * W2, bv + 2 * b2, EPS)
+    parts = orc.post_proj(y, gam, bet, Wo, bv, EPS) + 2 * orc.post_proj(y, gam, bet, W2, b2, EPS)
+    np.testing.assert_allclose(lin, parts, rtol=1e-10, atol=1e-10)
+
+
+def test_post_proj_rows_independent(orc):
+    """Any subset of rows gives the same rows (the sampled full-size checks
+    rely on it)."""
+    r = _rng(6)
+    y = r.normal(size=(9, 16))
+    gam, bet, Wo = r.normal(size=16), r.normal(size=16), r.normal(size=(16, 5))
+    full = orc.post_proj(y, gam, bet, Wo)
+    np.testing.assert_array_equal(orc.post_proj(y[[2, 7, 3]], gam, bet, Wo), full[[2, 7, 3]])

@@ -88,6 +88,7 @@
 #ifndef TTT_H
 #define TTT_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -267,6 +268,47 @@ ttt_status ttt_mlp_prefill(const ttt_mlp_cfg *cfg, int32_t L, ttt_tensor XQ, ttt
 ttt_status ttt_mlp_decode(const ttt_mlp_cfg *cfg, int32_t T, ttt_tensor XQ, ttt_tensor XK, ttt_tensor XV,
                           ttt_eta eta, const float *ln_w, const float *ln_b, ttt_mlp_state *state,
                           ttt_tensor out, void *stream);
+
+/* ---- Post-norm and output projection: the steps after the layer ----
+ *
+ * "代码连连看——TTT", TTTBase.forward: after the scan the heads' outputs are
+ * concatenated to [B, L, width] (width = H * D), then go through post_norm, a
+ * LayerNorm over the width, and o_proj, a linear map.  With y that output as
+ * M = B * L rows of K = width values (the prefill's out written with
+ * sB = L*H*D, sH = D, sL = H*D is this layout) and Wo [K, N]:
+ *   out[m, :] = ((y[m, :] - mean_m) / sqrt(var_m + eps) * gamma + beta) Wo + bias
+ * (var_m the population variance of row m).  The pages do not show the
+ * constructors of post_norm and o_proj; bias may be NULL (none).
+ *
+ * Arithmetic: bf16 operands, fp32 accumulation.  The weights enter as
+ * W' = bf16(diag(gamma) Wo) with c1 = column sums of W' and
+ * c2 = beta^T Wo + bias, and out = r (y W') - r mean c1 + c2 per row, which is
+ * the LayerNorm followed by the product with W'.  The row statistics are
+ * sums over the bf16 values of y in fp32 (mean of squares minus squared mean:
+ * rows whose mean is many standard deviations from zero lose precision).
+ *
+ * ttt_post_proj_prepared_bytes(K, N): size of the prepared-weights buffer,
+ * K * N * 2 + N * 8 bytes (0 for K or N <= 0).
+ *
+ * ttt_post_proj_prepare: forms the prepared weights from gamma, beta [K],
+ * Wo [K, N] row-major and bias [N] (or NULL), fp32 device arrays, into
+ * `prepared` (device, 16-byte aligned, caller-owned, prepared_bytes long),
+ * enqueued on `stream`; done once per weight set.  K must be a positive
+ * multiple of 64 and N of 256 (TTT_ERR_SHAPE); NULL pointers give
+ * TTT_ERR_NULL; `prepared` overlapping an input gives TTT_ERR_ALIAS.
+ *
+ * ttt_post_proj: y [M, K] bf16 device rows of stride ldy elements (ldy >= K,
+ * a multiple of 8; y 16-byte aligned), `prepared` from ttt_post_proj_prepare
+ * with the same K, N, out [M, N] device rows of stride ldo (>= N) in
+ * out_dtype (TTT_F32 or TTT_BF16), eps > 0.  Enqueued on `stream`; reads y
+ * and prepared, writes out only.  Errors as above, plus TTT_ERR_DTYPE for
+ * out_dtype, TTT_ERR_ALIGN for y / prepared / out alignment, TTT_ERR_ALIAS
+ * when out overlaps y or prepared, TTT_ERR_HIP when a launch fails. */
+size_t ttt_post_proj_prepared_bytes(int32_t K, int32_t N);
+ttt_status ttt_post_proj_prepare(int32_t K, int32_t N, const float *gamma, const float *beta, const float *Wo,
+                                 const float *bias, void *prepared, void *stream);
+ttt_status ttt_post_proj(int32_t M, int32_t K, int32_t N, const void *y, int64_t ldy, float eps,
+                         const void *prepared, void *out, int64_t ldo, int32_t out_dtype, void *stream);
 
 const char *ttt_status_string(ttt_status s);
 const char *ttt_last_error(void);

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "lib", "libttt.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["linear_token.hip", "linear_dual.hip", "mlp_dual.hip", "mlp_token.hip"]
+HIP_SOURCES = ["linear_token.hip", "linear_dual.hip", "mlp_dual.hip", "mlp_token.hip", "post_proj.hip"]
 CXX_SOURCES = ["ttt_host.cpp"]
 
 COMMON = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,

@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -473,6 +474,76 @@ ttt_status ttt_mlp_decode(const ttt_mlp_cfg *cfg, int32_t T, ttt_tensor XQ, ttt_
                           ttt_eta eta, const float *ln_w, const float *ln_b, ttt_mlp_state *state, ttt_tensor out,
                           void *stream) {
     return mlp_call(Mode::Decode, cfg, T, Act{XQ, XK, XV, out, eta, ln_w, ln_b}, state, stream);
+}
+
+size_t ttt_post_proj_prepared_bytes(int32_t K, int32_t N) {
+    if (K <= 0 || N <= 0) return 0;
+    return (size_t)K * (size_t)N * 2 + (size_t)N * 8;
+}
+
+ttt_status ttt_post_proj_prepare(int32_t K, int32_t N, const float *gamma, const float *beta, const float *Wo,
+                                 const float *bias, void *prepared, void *stream) {
+    if (!gamma || !beta || !Wo || !prepared) return fail(TTT_ERR_NULL, "gamma / beta / Wo / prepared is NULL");
+    if (K < 64 || K % 64 || N < 256 || N % 256)
+        return fail(TTT_ERR_SHAPE, "K = %d must be a positive multiple of 64 and N = %d of 256", K, N);
+    if (!aligned16(prepared)) return fail(TTT_ERR_ALIGN, "prepared is not 16-byte aligned");
+    const Range rp = flat_range(prepared, (int64_t)ttt_post_proj_prepared_bytes(K, N), 1);
+    const Range ins[] = {flat_range(gamma, K, 4), flat_range(beta, K, 4), flat_range(Wo, (int64_t)K * N, 4),
+                         bias ? flat_range(bias, N, 4) : Range{0, 0}};
+    for (const Range &r : ins)
+        if (overlap(rp, r)) return fail(TTT_ERR_ALIAS, "prepared overlaps an input");
+    ttt_status s;
+    if ((s = take_pending_error())) return s;
+    PostPrepArgs a{};
+    a.gamma = gamma;
+    a.beta = beta;
+    a.Wo = Wo;
+    a.bias = bias;
+    a.Wt = static_cast<__bf16 *>(prepared);
+    a.c1 = reinterpret_cast<float *>(static_cast<char *>(prepared) + (size_t)K * N * 2);
+    a.c2 = a.c1 + N;
+    a.K = K;
+    a.N = N;
+    if (hipError_t e = launch_post_proj_prepare(a, reinterpret_cast<hipStream_t>(stream)); e != hipSuccess)
+        return hip_fail(e, "post_proj prepare");
+    return ok();
+}
+
+ttt_status ttt_post_proj(int32_t M, int32_t K, int32_t N, const void *y, int64_t ldy, float eps,
+                         const void *prepared, void *out, int64_t ldo, int32_t out_dtype, void *stream) {
+    if (!y || !prepared || !out) return fail(TTT_ERR_NULL, "y / prepared / out is NULL");
+    if (M < 1 || K < 64 || K % 64 || N < 256 || N % 256)
+        return fail(TTT_ERR_SHAPE, "M = %d must be >= 1, K = %d a positive multiple of 64, N = %d of 256", M, K, N);
+    if (ldy < K || ldo < N) return fail(TTT_ERR_SHAPE, "row strides ldy = %lld < K or ldo = %lld < N",
+                                        (long long)ldy, (long long)ldo);
+    if (!dtype_valid(out_dtype)) return fail(TTT_ERR_DTYPE, "out_dtype %d is not TTT_F32 or TTT_BF16", out_dtype);
+    if (!(eps > 0.f) || !std::isfinite(eps)) return fail(TTT_ERR_SHAPE, "eps must be finite and > 0");
+    const size_t eo = dtype_size(out_dtype);
+    if (!aligned16(y) || ldy % 8) return fail(TTT_ERR_ALIGN, "y must be 16-byte aligned with ldy a multiple of 8");
+    if (!aligned16(prepared)) return fail(TTT_ERR_ALIGN, "prepared is not 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(out) % eo) return fail(TTT_ERR_ALIGN, "out is not aligned to its element");
+    const Range ry = flat_range(y, (int64_t)(M - 1) * ldy + K, 2);
+    const Range rp = flat_range(prepared, (int64_t)ttt_post_proj_prepared_bytes(K, N), 1);
+    const Range ro = flat_range(out, (int64_t)(M - 1) * ldo + N, eo);
+    if (overlap(ro, ry) || overlap(ro, rp)) return fail(TTT_ERR_ALIAS, "out overlaps y or the prepared weights");
+    ttt_status s;
+    if ((s = take_pending_error())) return s;
+    PostArgs a{};
+    a.y = static_cast<const __bf16 *>(y);
+    a.ldy = ldy;
+    a.Wt = static_cast<const __bf16 *>(prepared);
+    a.c1 = reinterpret_cast<const float *>(static_cast<const char *>(prepared) + (size_t)K * N * 2);
+    a.c2 = a.c1 + N;
+    a.out = out;
+    a.ldo = ldo;
+    a.M = M;
+    a.K = K;
+    a.N = N;
+    a.eps = eps;
+    if (hipError_t e = launch_post_proj(a, out_dtype == TTT_BF16, reinterpret_cast<hipStream_t>(stream));
+        e != hipSuccess)
+        return hip_fail(e, "post_proj");
+    return ok();
 }
 
 }  // extern "C"

@@ -20,7 +20,8 @@ TTT_F32, TTT_BF16 = 0, 1
 TTT_GRAD_DENSE, TTT_GRAD_ROWS = 0, 1
 
 EXPORTS = ["ttt_linear_state_init", "ttt_linear_prefill", "ttt_linear_decode", "ttt_mlp_state_init",
-           "ttt_mlp_prefill", "ttt_mlp_decode", "ttt_status_string", "ttt_last_error"]
+           "ttt_mlp_prefill", "ttt_mlp_decode", "ttt_post_proj_prepared_bytes", "ttt_post_proj_prepare",
+           "ttt_post_proj", "ttt_status_string", "ttt_last_error"]
 
 
 class ttt_tensor(ctypes.Structure):
@@ -85,8 +86,14 @@ def load():
     lib.ttt_mlp_prefill.argtypes = [P(ttt_mlp_cfg), c_int32, ttt_tensor, ttt_tensor, ttt_tensor, ttt_eta, c_void_p,
                                     c_void_p, P(ttt_mlp_state), ttt_tensor, c_void_p]
     lib.ttt_mlp_decode.argtypes = lib.ttt_mlp_prefill.argtypes
+    lib.ttt_post_proj_prepared_bytes.argtypes = [c_int32, c_int32]
+    lib.ttt_post_proj_prepared_bytes.restype = ctypes.c_size_t
+    lib.ttt_post_proj_prepare.argtypes = [c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                          c_void_p]
+    lib.ttt_post_proj.argtypes = [c_int32, c_int32, c_int32, c_void_p, c_int64, c_float, c_void_p, c_void_p,
+                                  c_int64, c_int32, c_void_p]
     for f in ("ttt_linear_state_init", "ttt_linear_prefill", "ttt_linear_decode", "ttt_mlp_state_init",
-              "ttt_mlp_prefill", "ttt_mlp_decode"):
+              "ttt_mlp_prefill", "ttt_mlp_decode", "ttt_post_proj_prepare", "ttt_post_proj"):
         getattr(lib, f).restype = c_int32
     _lib = lib
     return lib
@@ -270,3 +277,20 @@ def ttt_status_string(status: int) -> str:
 
 def ttt_last_error() -> str:
     return load().ttt_last_error().decode()
+
+
+def ttt_post_proj_prepared_bytes(K, N) -> int:
+    return int(load().ttt_post_proj_prepared_bytes(int(K), int(N)))
+
+
+def ttt_post_proj_prepare(K, N, gamma, beta, Wo, bias, prepared, stream=None):
+    """gamma, beta [K], Wo [K, N] (row-major), bias [N] or None: fp32 device
+    tensors; prepared: a device buffer of ttt_post_proj_prepared_bytes(K, N)."""
+    _check(load().ttt_post_proj_prepare(int(K), int(N), _ptr(gamma), _ptr(beta), _ptr(Wo), _ptr(bias),
+                                        _ptr(prepared), _stream(stream)))
+
+
+def ttt_post_proj(M, K, N, y, ldy, eps, prepared, out, ldo, out_dtype="f32", stream=None):
+    """y [M, K] bf16 rows of stride ldy; out [M, N] rows of stride ldo."""
+    _check(load().ttt_post_proj(int(M), int(K), int(N), _ptr(y), int(ldy), float(eps), _ptr(prepared), _ptr(out),
+                                int(ldo), dtype_code(out_dtype), _stream(stream)))

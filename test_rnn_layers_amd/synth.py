@@ -18,6 +18,14 @@ heads x 64 for the 125m style, 1024 = 16 x 64 for 350m, 2048 = 32 x 64 for the
   * W0 ~ N(0, 0.02^2) per head, b0 = 0 (the TTTLinear init on the pages),
     LayerNorm gamma = 1, beta = 0 — unless ``rich=True``, which draws
     non-trivial b0, gamma, beta so that parity checks exercise every term.
+
+Post-norm and output projection (``make_post_proj_inputs``): y [M, K] the
+layer output as bf16 rows, N(offset_m, spread_m^2) with a per-row offset and
+spread (drawn once per row) so that the LayerNorm has work to do; gamma =
+1 + 0.2 N(0, 1), beta = 0.2 N(0, 1); Wo ~ N(0, 0.02^2) [K, N]; bias 0.05 N(0, 1)
+or none.  With ``exact_weights=True`` gamma is a random power of two in
+{+-1/2, +-1, +-2} and Wo is rounded to bf16, so that gamma * Wo is exactly
+representable in bf16.
 """
 from __future__ import annotations
 
@@ -101,3 +109,21 @@ def make_inputs(B: int, H: int, L: int, *, D: int = D_HEAD, dtype: str = "f32", 
 def workload_inputs(w: Workload) -> dict:
     return make_inputs(w.B, w.H, w.L, dtype=w.dtype, seed=w.seed,
                        mlp_hidden=MLP_HIDDEN if w.kind in ("mlp", "mlp_decode") else 0)
+
+
+def make_post_proj_inputs(M: int, K: int, N: int, *, seed: int = 0, bias: bool = False, offset: float = 1.0,
+                          exact_weights: bool = False) -> dict:
+    """y [M, K] bf16; gamma, beta [K], Wo [K, N], bias [N] (or None) fp32; CPU tensors."""
+    g = torch.Generator().manual_seed(seed)
+    mean = offset * torch.randn((M, 1), generator=g, dtype=torch.float32)
+    spread = 0.5 + torch.rand((M, 1), generator=g, dtype=torch.float32) * 1.5
+    y = (mean + spread * torch.randn((M, K), generator=g, dtype=torch.float32)).to(torch.bfloat16)
+    gamma = 1.0 + 0.2 * torch.randn(K, generator=g, dtype=torch.float32)
+    beta = 0.2 * torch.randn(K, generator=g, dtype=torch.float32)
+    Wo = 0.02 * torch.randn((K, N), generator=g, dtype=torch.float32)
+    bv = 0.05 * torch.randn(N, generator=g, dtype=torch.float32) if bias else None
+    if exact_weights:
+        pick = torch.randint(0, 6, (K,), generator=g)
+        gamma = torch.tensor([-2.0, -1.0, -0.5, 0.5, 1.0, 2.0])[pick]
+        Wo = Wo.to(torch.bfloat16).to(torch.float32)
+    return {"y": y, "gamma": gamma, "beta": beta, "Wo": Wo, "bias": bv}

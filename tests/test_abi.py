@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "ttt.h")
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const char \*|ttt_status )\s*(ttt_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const char \*|ttt_status |size_t )\s*(ttt_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_entry_points():
@@ -221,3 +221,57 @@ def test_c_example_is_built_against_the_header():
     und = subprocess.run(["nm", "-D", "--undefined-only", C_EXAMPLE], capture_output=True, text=True).stdout
     for sym in ("ttt_linear_state_init", "ttt_linear_prefill", "ttt_linear_decode", "ttt_last_error"):
         assert sym in und, sym
+
+
+# --- post-norm and output projection
+def _pp_args(**over):
+    a = dict(M=300, K=128, N=256, y=_addr(0), ldy=128, eps=1e-5, prepared=_addr(1), out=_addr(2), ldo=256,
+             out_dtype=T.TTT_F32, stream=None)
+    a.update(over)
+    return a
+
+
+def _pp_call(a):
+    lib = T.load()
+    return lib.ttt_post_proj(a["M"], a["K"], a["N"], a["y"], a["ldy"], a["eps"], a["prepared"], a["out"],
+                             a["ldo"], a["out_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("label,over,expect", [
+    ("y NULL", dict(y=0), "TTT_ERR_NULL"),
+    ("prepared NULL", dict(prepared=0), "TTT_ERR_NULL"),
+    ("out NULL", dict(out=0), "TTT_ERR_NULL"),
+    ("M = 0", dict(M=0), "TTT_ERR_SHAPE"),
+    ("K not a multiple of 64", dict(K=96, ldy=96), "TTT_ERR_SHAPE"),
+    ("N not a multiple of 256", dict(N=128, ldo=128), "TTT_ERR_SHAPE"),
+    ("ldy < K", dict(ldy=64), "TTT_ERR_SHAPE"),
+    ("ldo < N", dict(ldo=255), "TTT_ERR_SHAPE"),
+    ("eps = 0", dict(eps=0.0), "TTT_ERR_SHAPE"),
+    ("out dtype", dict(out_dtype=7), "TTT_ERR_DTYPE"),
+    ("y misaligned", dict(y=_addr(0) + 2), "TTT_ERR_ALIGN"),
+    ("ldy not a multiple of 8", dict(ldy=132), "TTT_ERR_ALIGN"),
+    ("prepared misaligned", dict(prepared=_addr(1) + 8), "TTT_ERR_ALIGN"),
+    ("out misaligned", dict(out=_addr(2) + 2), "TTT_ERR_ALIGN"),
+    ("out overlaps y", dict(out=_addr(0) + 4096), "TTT_ERR_ALIAS"),
+    ("out overlaps prepared", dict(out=_addr(1) + 16), "TTT_ERR_ALIAS"),
+])
+def test_post_proj_error_paths(label, over, expect):
+    s = _pp_call(_pp_args(**over))
+    assert T.STATUS_NAMES[s] == expect, (label, T.ttt_last_error())
+    assert T.ttt_last_error()
+
+
+def test_post_proj_prepare_errors():
+    lib = T.load()
+    K, N = 128, 256
+    assert T.ttt_post_proj_prepared_bytes(K, N) == K * N * 2 + N * 8
+    assert T.ttt_post_proj_prepared_bytes(0, N) == 0
+    args = dict(K=K, N=N, gamma=_addr(0), beta=_addr(1), Wo=_addr(2), bias=None, prepared=_addr(3))
+    cases = [(dict(gamma=0), "TTT_ERR_NULL"), (dict(Wo=0), "TTT_ERR_NULL"), (dict(prepared=0), "TTT_ERR_NULL"),
+             (dict(K=100), "TTT_ERR_SHAPE"), (dict(N=300), "TTT_ERR_SHAPE"), (dict(prepared=_addr(3) + 4),
+                                                                             "TTT_ERR_ALIGN"),
+             (dict(prepared=_addr(2) + 64), "TTT_ERR_ALIAS"), (dict(bias=_addr(3) + 32), "TTT_ERR_ALIAS")]
+    for over, expect in cases:
+        a = dict(args, **over)
+        s = lib.ttt_post_proj_prepare(a["K"], a["N"], a["gamma"], a["beta"], a["Wo"], a["bias"], a["prepared"], None)
+        assert T.STATUS_NAMES[s] == expect, (over, T.ttt_last_error())

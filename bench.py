@@ -12,6 +12,9 @@ Other workloads (``--workload``):
                decode calls; the value is decode tokens/s
   mlp_decode_350m  TTT-MLP, B = 16, H = 16: prefill 512 tokens, then 64
                single-token decode calls; the value is decode tokens/s
+  post_proj_1b the steps after the layer: post-norm LayerNorm and output
+               projection of the 1B-style layer output (M = B L = 32768
+               rows, width 2048 -> 2048), bf16 in and out; tokens/s
 
 Prints one JSON line: whole-step throughput, the roofline of the dominant
 kernel (its launches timed with HIP events on the stream they run on), and
@@ -106,7 +109,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="linear_1b",
-                    choices=["linear_1b", "linear_125m", "mlp_350m", "decode_1b", "mlp_decode_350m"])
+                    choices=["linear_1b", "linear_125m", "mlp_350m", "decode_1b", "mlp_decode_350m",
+                             "post_proj_1b"])
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--rope", action="store_true", help="rotary on for a linear workload that has it off")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -674,12 +678,85 @@ def bench_mlp_decode(args, w):
     return res
 
 
+# post-norm + output projection of the 1B-style layer: M = B L rows of the
+# layer output, K = width = 32 heads x 64, N = the model width
+POST_PROJ_1B = dict(name="post_proj_1b_M32768_K2048_N2048_bf16", M=4 * 8192, K=2048, N=2048, seed=1240)
+
+
+def cpu_post_proj(inp, budget):
+    """The oracle on blocks of 64 rows of the same inputs, cycled, until the
+    budget is spent."""
+    import oracle
+
+    y = inp["y"].double().numpy()
+    g, b, W = (inp[n].double().numpy() for n in ("gamma", "beta", "Wo"))
+    M = y.shape[0]
+    done, dt = 0, 0.0
+    while done == 0 or dt < budget:
+        r0 = (done * 64) % M
+        t0 = time.perf_counter()
+        oracle.post_proj(y[r0:r0 + 64], g, b, W, None, 1e-5)
+        dt += time.perf_counter() - t0
+        done += 1
+    return {"value": done * 64 / dt, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"{done} blocks of 64 rows of the {M}-row workload, fp64, {dt:.1f} s"}
+
+
+def bench_post_proj(args):
+    import torch
+
+    from test_rnn_layers_amd import libttt
+    from test_rnn_layers_amd.synth import make_post_proj_inputs
+
+    c = POST_PROJ_1B
+    M, K, N = c["M"], c["K"], c["N"]
+    dev = "cuda"
+    inp = make_post_proj_inputs(M, K, N, seed=c["seed"])
+    ys = [inp["y"].to(dev).contiguous(), inp["y"].flip(0).to(dev).contiguous()]  # two resident sets (MALL)
+    g, b, W = (inp[n].to(dev).contiguous() for n in ("gamma", "beta", "Wo"))
+    prepared = torch.empty(libttt.ttt_post_proj_prepared_bytes(K, N), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    libttt.ttt_post_proj_prepare(K, N, g, b, W, None, prepared, stream)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    tm = Timer(stream)
+
+    def step(i, timed):
+        if timed:
+            tm.start("proj")
+        libttt.ttt_post_proj(M, K, N, ys[i % 2], K, 1e-5, prepared, out, N, "bf16", stream)
+        if timed:
+            tm.stop("proj")
+
+    elapsed = run_steps(args, step)
+    flops = 2 * M * K * N
+    res = {"metric": f"post-norm + output projection tokens/sec ({c['name']})", "value": M * args.steps / elapsed,
+           "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": elapsed * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16 MFMA operands (gamma folded into the weights), fp32 accumulate",
+           "data": "synthetic: seeded bf16 rows N(m, s^2) with per-row m, s; gamma, beta near 1, 0; Wo ~ N(0, 0.02^2)",
+           "config": {"workload": c["name"], "M": M, "K": K, "N": N, "in_dtype": "bf16", "out_dtype": "bf16",
+                      "parallelism": "single GPU, 256x256 output tiles"}}
+    res["roofline"] = roofline("post_proj_kernel", c["name"], bound="mfma", amount=flops,
+                               kernel_ms=stats(tm.ms("proj")),
+                               per_unit=f"2 K N = {2 * K * N} MFMA flops per row",
+                               units=f"{M} rows")
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = with_thread_sweep(cpu_post_proj, args.cpu_seconds, inp)
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); the (batch, head) "
               "chains are independent, so more GPUs would each take a share of the batch", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "post_proj_1b":
+        res = bench_post_proj(args)
+        if args.copy_probe_mb:
+            copy_probe(args.copy_probe_mb)
+        print(json.dumps(res), flush=True)
+        return
     from test_rnn_layers_amd.synth import WORKLOADS
 
     w = {"linear_125m": WORKLOADS[1], "linear_1b": WORKLOADS[2], "mlp_350m": WORKLOADS[3],

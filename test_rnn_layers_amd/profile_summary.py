@@ -34,7 +34,8 @@ import statistics
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 KERNEL_SOURCES = {"linear_dual_kernel": "linear_dual.hip", "mlp_dual_kernel": "mlp_dual.hip",
-                  "linear_token_kernel": "linear_token.hip", "mlp_token_kernel": "mlp_token.hip"}
+                  "linear_token_kernel": "linear_token.hip", "mlp_token_kernel": "mlp_token.hip",
+                  "post_proj_kernel": "post_proj.hip"}
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 MFMA_JSON = os.path.join(ROOT, "profiles", "mfma.json")
 SIMDS_PER_CU = 4

@@ -299,8 +299,9 @@ ttt_status ttt_mlp_decode(const ttt_mlp_cfg *cfg, int32_t T, ttt_tensor XQ, ttt_
  *
  * ttt_post_proj: y [M, K] bf16 device rows of stride ldy elements (ldy >= K,
  * a multiple of 8; y 16-byte aligned), `prepared` from ttt_post_proj_prepare
- * with the same K, N, out [M, N] device rows of stride ldo (>= N) in
- * out_dtype (TTT_F32 or TTT_BF16), eps > 0.  Enqueued on `stream`; reads y
+ * with the same K, N, out [M, N] device rows of stride ldo (>= N; out
+ * 16-byte aligned and ldo a multiple of 16 bytes) in out_dtype (TTT_F32 or
+ * TTT_BF16), eps > 0.  Enqueued on `stream`; reads y
  * and prepared, writes out only.  Errors as above, plus TTT_ERR_DTYPE for
  * out_dtype, TTT_ERR_ALIGN for y / prepared / out alignment, TTT_ERR_ALIAS
  * when out overlaps y or prepared, TTT_ERR_HIP when a launch fails. */

@@ -174,23 +174,43 @@ __global__ __launch_bounds__(512, 1) void post_proj_kernel(PostArgs p) {
     }
     __syncthreads();
 
-    // out = r (y . W') - r mean c1 + c2
+    // out = r (y . W') - r mean c1 + c2, staged through LDS in two passes of
+    // 128 rows (the waves of row block p write their tiles, then every thread
+    // stores 16-byte pieces of whole rows)
+    constexpr int OP = 256 + 16 / (int)sizeof(Tout);  // staging row pitch (elements)
+    Tout *stage = reinterpret_cast<Tout *>(smem_raw);   // [128][OP], over the A/B stages
     Tout *out = (Tout *)p.out;
+    float c1[4], c2[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int col = n0 + wn * 64 + 16 * j + n;
-        const float c1 = p.c1[col], c2 = p.c2[col];
+        c1[j] = p.c1[col];
+        c2[j] = p.c2[col];
+    }
+    for (int pass = 0; pass < 2; ++pass) {
+        if (wm == pass) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int row = wm * 128 + 16 * i + 4 * g + jj, m = m0 + row;
-                if (m < p.M) {
-                    const float r = sm.r[row];
-                    const float v = fmaf(r, acc[i][j][jj], fmaf(-r * sm.mu[row], c1, c2));
-                    out[(int64_t)m * p.ldo + col] = (Tout)v;
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int rl = 16 * i + 4 * g + jj, row = 128 * pass + rl;
+                    const float r = sm.r[row], nmr = -r * sm.mu[row];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        stage[rl * OP + wn * 64 + 16 * j + n] = (Tout)fmaf(r, acc[i][j][jj], fmaf(nmr, c1[j], c2[j]));
                 }
-            }
+        }
+        __syncthreads();
+        constexpr int per_row = 256 * (int)sizeof(Tout) / 16;  // 16-byte pieces per row
+#pragma unroll 4
+        for (int c = t; c < 128 * per_row; c += 512) {
+            const int rl = c / per_row, piece = c % per_row;
+            const int m = m0 + 128 * pass + rl;
+            if (m < p.M)
+                *(uint4 *)((char *)(out + (int64_t)m * p.ldo + n0) + 16 * piece) =
+                    *(const uint4 *)((const char *)(stage + rl * OP) + 16 * piece);
+        }
+        __syncthreads();
     }
 }
 

@@ -521,7 +521,8 @@ ttt_status ttt_post_proj(int32_t M, int32_t K, int32_t N, const void *y, int64_t
     const size_t eo = dtype_size(out_dtype);
     if (!aligned16(y) || ldy % 8) return fail(TTT_ERR_ALIGN, "y must be 16-byte aligned with ldy a multiple of 8");
     if (!aligned16(prepared)) return fail(TTT_ERR_ALIGN, "prepared is not 16-byte aligned");
-    if (reinterpret_cast<uintptr_t>(out) % eo) return fail(TTT_ERR_ALIGN, "out is not aligned to its element");
+    if (!aligned16(out) || (ldo * (int64_t)eo) % 16)
+        return fail(TTT_ERR_ALIGN, "out must be 16-byte aligned with rows a multiple of 16 bytes apart");
     const Range ry = flat_range(y, (int64_t)(M - 1) * ldy + K, 2);
     const Range rp = flat_range(prepared, (int64_t)ttt_post_proj_prepared_bytes(K, N), 1);
     const Range ro = flat_range(out, (int64_t)(M - 1) * ldo + N, eo);

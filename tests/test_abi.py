@@ -251,7 +251,8 @@ def _pp_call(a):
     ("y misaligned", dict(y=_addr(0) + 2), "TTT_ERR_ALIGN"),
     ("ldy not a multiple of 8", dict(ldy=132), "TTT_ERR_ALIGN"),
     ("prepared misaligned", dict(prepared=_addr(1) + 8), "TTT_ERR_ALIGN"),
-    ("out misaligned", dict(out=_addr(2) + 2), "TTT_ERR_ALIGN"),
+    ("out misaligned", dict(out=_addr(2) + 4), "TTT_ERR_ALIGN"),
+    ("ldo not a multiple of 16 bytes", dict(ldo=258), "TTT_ERR_ALIGN"),
     ("out overlaps y", dict(out=_addr(0) + 4096), "TTT_ERR_ALIAS"),
     ("out overlaps prepared", dict(out=_addr(1) + 16), "TTT_ERR_ALIAS"),
 ])

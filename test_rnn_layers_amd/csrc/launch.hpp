@@ -48,28 +48,6 @@ struct MlpArgs {
     int32_t grad_rows;  // W1_grad / W2_grad hold the open rows [k | eta g1], [x2 | eta g2]
 };
 
-// Post-norm LayerNorm and output projection of the layer output (post_proj.hip).
-struct PostPrepArgs {
-    const float *gamma, *beta;  // [K]
-    const float *Wo;            // [K, N]
-    const float *bias;          // [N] or nullptr
-    __bf16 *Wt;                 // W' = diag(gamma) Wo, transposed: [N, K]
-    float *c1, *c2;             // [N]
-    int32_t K, N;
-};
-struct PostArgs {
-    const __bf16 *y;  // [M, K] rows of stride ldy
-    int64_t ldy;
-    const __bf16 *Wt;
-    const float *c1, *c2;
-    void *out;        // [M, N] rows of stride ldo
-    int64_t ldo;
-    int32_t M, K, N;
-    float eps;
-};
-hipError_t launch_post_proj_prepare(const PostPrepArgs &a, hipStream_t s);
-hipError_t launch_post_proj(const PostArgs &a, int out_bf16, hipStream_t s);
-
 hipError_t launch_linear_token(const LinearArgs &a, int in_bf16, int out_bf16, hipStream_t s);
 hipError_t launch_linear_dual(const LinearArgs &a, int in_bf16, int out_bf16, hipStream_t s);
 hipError_t launch_mlp_dual(const MlpArgs &a, int in_bf16, int out_bf16, hipStream_t s);

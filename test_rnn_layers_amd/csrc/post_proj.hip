@@ -33,6 +33,7 @@
 
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "post_proj.hpp"
 
 namespace ttt {
 namespace {

@@ -20,6 +20,7 @@
 #include <vector>
 
 #include "launch.hpp"
+#include "post_proj.hpp"
 #include "ttt.h"
 
 using namespace ttt;

@@ -46,7 +46,8 @@ XCCS = 8  # GRBM_GUI_ACTIVE is reported once per XCC; the dispatch's cycles are 
 def source_digest(kernel: str) -> str:
     """sha256 over the kernel's source file and the headers it includes."""
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[kernel], "device_common.hpp", "launch.hpp", "gelu.hpp"):
+    extra = ("post_proj.hpp",) if kernel == "post_proj_kernel" else ()
+    for f in (KERNEL_SOURCES[kernel], "device_common.hpp", "launch.hpp", "gelu.hpp") + extra:
         with open(os.path.join(PKG, "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()

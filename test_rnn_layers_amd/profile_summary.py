@@ -175,7 +175,7 @@ def mfma_summary(d, kernel, workload, workgroups, flops, cmd):
     return "\n".join(lines) + "\n"
 
 
-def sq_summary(dirs, kernel, cmd, blocks_per_chain):
+def sq_summary(dirs, kernel, cmd, blocks_per_chain, cus=0):
     """Shader-sequencer counters of one kernel (SQ_*), summed over its
     dispatches and divided by the dispatch count, with per-wave figures.
     SQ_WAVE_CYCLES, SQ_BUSY_CYCLES and the SQ_ACTIVE_* / SQ_WAIT_* counters
@@ -208,7 +208,16 @@ def sq_summary(dirs, kernel, cmd, blocks_per_chain):
                              f"SQ_WAVE_CYCLES per wave)")
         if "SQ_LDS_BANK_CONFLICT" in m and m.get("SQ_ACTIVE_INST_LDS"):
             lines.append(f"- SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS = "
-                         f"{m['SQ_LDS_BANK_CONFLICT'] / m['SQ_ACTIVE_INST_LDS']:.2f}")
+                         f"{m['SQ_LDS_BANK_CONFLICT'] / m['SQ_ACTIVE_INST_LDS']:.2f} (mixed units: the first counts "
+                         f"cycles the LDS is stalled, the second quad-cycles of each wave)")
+    if "SQ_LDS_BANK_CONFLICT" in m and m.get("SQ_LDS_IDX_ACTIVE"):
+        lines.append(f"- SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE = "
+                     f"{m['SQ_LDS_BANK_CONFLICT'] / m['SQ_LDS_IDX_ACTIVE']:.3f} (both cycles of the LDS: the share of "
+                     f"its busy cycles lost to bank conflicts)")
+    if "SQ_LDS_BANK_CONFLICT" in m and m.get("GRBM_GUI_ACTIVE") and cus:
+        cyc = m["GRBM_GUI_ACTIVE"] / XCCS
+        lines.append(f"- bank-conflict stall cycles per CU that holds a workgroup: "
+                     f"{m['SQ_LDS_BANK_CONFLICT'] / cus / cyc:.1%} of the dispatch ({cyc:.0f} cycles, {cus} CUs)")
     lines.append(f"- kernel source sha256 {source_digest(kernel)[:16]}...")
     return "\n".join(lines) + "\n"
 
@@ -233,6 +242,7 @@ def main():
     q.add_argument("dirs", nargs="+")
     q.add_argument("--kernel", required=True)
     q.add_argument("--blocks-per-chain", type=int, default=0, help="mini-batches per chain (per-mini-batch figures)")
+    q.add_argument("--cus", type=int, default=0, help="CUs that hold a workgroup (per-CU figures)")
     q.add_argument("--cmd", required=True)
     q.add_argument("--out", required=True)
     f = sub.add_parser("mfma")
@@ -247,7 +257,7 @@ def main():
     if a.cmd_name == "stats":
         text = stats_summary(a.dir, a.kernel, a.cmd)
     elif a.cmd_name == "sq":
-        text = sq_summary(a.dirs, a.kernel, a.cmd, a.blocks_per_chain)
+        text = sq_summary(a.dirs, a.kernel, a.cmd, a.blocks_per_chain, a.cus)
     elif a.cmd_name == "mfma":
         text = mfma_summary(a.dir, a.kernel, a.workload, a.workgroups, a.flops, a.cmd)
     else:

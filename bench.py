@@ -740,9 +740,32 @@ def bench_post_proj(args):
                                kernel_ms=stats(tm.ms("proj")),
                                per_unit=f"2 K N = {2 * K * N} MFMA flops per row",
                                units=f"{M} rows")
+    res["library_gemm"] = library_gemm(ys, prepared, M, K, N)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = with_thread_sweep(cpu_post_proj, args.cpu_seconds, inp)
     return res
+
+
+def library_gemm(ys, prepared, M, K, N, reps=10):
+    """Context for the projection's roofline: the vendor library's plain GEMM
+    (torch.nn.functional.linear, bf16 in and out) on the same y and W' operands,
+    without the LayerNorm fold.  Timed after, and apart from, the product path."""
+    import torch
+
+    Wt = prepared[:N * K * 2].view(torch.bfloat16).view(N, K)
+    for i in range(3):
+        torch.nn.functional.linear(ys[i % 2], Wt)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(reps):
+        torch.nn.functional.linear(ys[i % 2], Wt)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"what": "torch.nn.functional.linear (vendor BLAS) on the same bf16 y and W' operands, bf16 out, "
+                    "no LayerNorm fold; not part of the measured path",
+            "us_mean": round(ms * 1e3, 1), "tflops": round(2 * M * K * N / (ms * 1e-3) / 1e12, 1)}
 
 
 def main():

@@ -50,20 +50,49 @@ struct PSmem {
     float mu[BM], r[BM];  // row mean and 1 / sqrt(var + eps)
 };
 
-// W'^T [N][K] bf16, c1, c2 [N]
-__global__ void post_proj_prepare_kernel(PostPrepArgs p) {
-    const int col = blockIdx.x * blockDim.x + threadIdx.x;
-    if (col >= p.N) return;
+// W'^T [N][K] bf16, c1, c2 [N].  A workgroup takes 16 columns: thread
+// (k-group kg, column cl) forms w = bf16(gamma_k Wo[k][col]) for k = kg mod 16
+// (the 16 columns of a row are one 64-byte read), the rounded values go
+// through LDS in chunks of 256 k so that every column's row of W'^T is
+// written in 16-byte pieces, and the fp64 column sums of the 16 k-groups are
+// added in a fixed order at the end.
+constexpr int kPrepCols = 16, kPrepChunk = 256;
+__global__ __launch_bounds__(256) void post_proj_prepare_kernel(PostPrepArgs p) {
+    __shared__ __align__(16) __bf16 tile[kPrepCols][kPrepChunk + 8];  // [column][k in the chunk]
+    __shared__ double red[2][16][kPrepCols];                           // [c1 | c2][k-group][column]
+    const int t = threadIdx.x, cl = t & 15, kg = t >> 4;
+    const int c0 = blockIdx.x * kPrepCols, col = c0 + cl;
     double c1 = 0.0, c2 = 0.0;
-    for (int k = 0; k < p.K; ++k) {
-        const float wo = p.Wo[(int64_t)k * p.N + col];
-        const __bf16 w = (__bf16)(p.gamma[k] * wo);
-        p.Wt[(int64_t)col * p.K + k] = w;
-        c1 += (double)(float)w;
-        c2 += (double)p.beta[k] * (double)wo;
+    for (int k0 = 0; k0 < p.K; k0 += kPrepChunk) {
+        const int kn = min(kPrepChunk, p.K - k0);  // a multiple of 64
+        for (int kk = kg; kk < kn; kk += 16) {
+            const int k = k0 + kk;
+            const float wo = p.Wo[(int64_t)k * p.N + col];
+            const __bf16 w = (__bf16)(p.gamma[k] * wo);
+            tile[cl][kk] = w;
+            c1 += (double)(float)w;
+            c2 += (double)p.beta[k] * (double)wo;
+        }
+        __syncthreads();
+        const int pieces = kn / 8;  // 16-byte pieces per column
+        for (int c = t; c < kPrepCols * pieces; c += 256) {
+            const int cc = c / pieces, pc = c % pieces;
+            *(uint4 *)(p.Wt + (int64_t)(c0 + cc) * p.K + k0 + 8 * pc) = *(const uint4 *)&tile[cc][8 * pc];
+        }
+        __syncthreads();
     }
-    p.c1[col] = (float)c1;
-    p.c2[col] = (float)(c2 + (p.bias ? (double)p.bias[col] : 0.0));
+    red[0][kg][cl] = c1;
+    red[1][kg][cl] = c2;
+    __syncthreads();
+    if (t < kPrepCols) {
+        double s1 = 0.0, s2 = 0.0;
+        for (int q = 0; q < 16; ++q) {
+            s1 += red[0][q][t];
+            s2 += red[1][q][t];
+        }
+        p.c1[c0 + t] = (float)s1;
+        p.c2[c0 + t] = (float)(s2 + (p.bias ? (double)p.bias[c0 + t] : 0.0));
+    }
 }
 
 template <typename Tout>
@@ -228,7 +257,7 @@ hipError_t launch_gemm(const PostArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_post_proj_prepare(const PostPrepArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(post_proj_prepare_kernel, dim3((a.N + 255) / 256), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(post_proj_prepare_kernel, dim3(a.N / kPrepCols), dim3(256), 0, s, a);  // N % 256 == 0
     return hipGetLastError();
 }
 

@@ -148,3 +148,33 @@ def test_after_the_layer():
     print(f"[post_proj_after_layer] layer output max-abs beyond half a bf16 ulp {dlayer.max():.3e}", flush=True)
     assert dlayer.max() <= 2e-2
     _check("post_proj_after_layer", pp, got, np.arange(B * L), exact=False)
+
+
+@pytest.mark.parametrize("shape", [(192, 512, True), (2048, 2048, False), (320, 256, True)])
+def test_prepared_weights(shape):
+    """The prepared buffer itself: W'^T [N][K] must be bf16(gamma_k Wo[k][n])
+    bit for bit (one fp32 product, rounded to nearest even), c1 the sum of
+    the rounded W' column (a sum of bf16 values, exact in fp64 here, so bit
+    for bit after the fp32 rounding) and c2 = beta^T Wo + bias to 1 ulp of
+    fp32 (fp64 sums of fp32 products in another order)."""
+    K, N, bias = shape
+    inp = make_post_proj_inputs(8, K, N, seed=71 + K, bias=bias)
+    dev = "cuda"
+    g, b, W = (inp[n].to(dev).contiguous() for n in ("gamma", "beta", "Wo"))
+    bv = inp["bias"].to(dev).contiguous() if bias else None
+    prepared = torch.empty(T.ttt_post_proj_prepared_bytes(K, N), dtype=torch.uint8, device=dev)
+    T.ttt_post_proj_prepare(K, N, g, b, W, bv, prepared)
+    torch.cuda.synchronize()
+    pc = prepared.cpu()
+    wt = pc[:N * K * 2].view(torch.bfloat16).view(N, K)
+    c1 = pc[N * K * 2:N * K * 2 + 4 * N].view(torch.float32).numpy()
+    c2 = pc[N * K * 2 + 4 * N:].view(torch.float32).numpy()
+    want = (inp["gamma"].float()[:, None] * inp["Wo"].float()).to(torch.bfloat16).t().contiguous()
+    assert torch.equal(wt.view(torch.int16), want.view(torch.int16))
+    c1_ref = want.double().sum(dim=1).numpy().astype(np.float32)
+    assert np.array_equal(c1, c1_ref)
+    c2_ref = inp["beta"].double().numpy() @ inp["Wo"].double().numpy()
+    if bias:
+        c2_ref = c2_ref + inp["bias"].double().numpy()
+    ulp = np.spacing(np.abs(c2_ref).astype(np.float32)).astype(np.float64)
+    assert (np.abs(c2.astype(np.float64) - c2_ref) <= ulp).all()
